@@ -1,0 +1,286 @@
+"""ctypes binding of libnvkv.so (argument marshalling only; every step runs in the HIP kernels).
+
+Each function takes torch tensors (torch provides device memory and the stream), checks dtype,
+device and shape, passes raw pointers to the C ABI declared in include/nvkv.h and raises
+RuntimeError on a non-zero status.  There is no CPU fallback: if the library is missing,
+importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvkv.so")
+
+HEAD_DIM = 128
+PAGE_SIZE = 16
+NVFP4_DATA_BYTES = 1024
+NVFP4_SCALE_BYTES = 128
+FP8_BYTES = 2048
+IN_BF16, IN_FP8 = 0, 1
+PREC_NVFP4, PREC_FP8 = 0, 1
+NVFP4_GLOBAL_DIVISOR = 2688.0   # 6 (E2M1 max) * 448 (E4M3 max)
+FP8_DIVISOR = 448.0
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "or `python bit_paged_kv_amd/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+EXPORTED = {
+    "nvkv_status_string": (ctypes.c_char_p, [_i]),
+    "nvkv_version": (_i, []),
+    "nvkv_global_scale_workspace_size": (_sz, []),
+    "nvkv_global_scale": (_i, [_p, _i, _f, _sz, _f, _p, _p, _sz, _p]),
+    "nvfp4_kv_quantize_append": (_i, [_p, _p, _i, _f, _f, _p, _i, _i, _i, _i, _f, _f, _p, _p, _p, _p, _p]),
+    "fp8_kv_quantize_append": (_i, [_p, _p, _p, _i, _i, _i, _i, _f, _f, _p, _p, _p]),
+    "nvkv_plan_decode": (_i, [_i, _i, _i, ctypes.c_longlong, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "nvkv_decode_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "nvfp4_paged_decode_attn": (_i, [_p, _p, _p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i,
+                                     _p, _p, _p, _p, _sz, _p]),
+    "fp8_paged_decode_attn": (_i, [_p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p, _p, _sz, _p]),
+    "nvkv_decode_layers": (_i, [_p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p, _sz, _p]),
+    "nvfp4_dequant_to_workspace": (_i, [_p, _p, _p, _p, _f, _f, _p, _i, _p, _p, _i, _i, _i, _i, _i, _f, _f, _p, _p,
+                                        _p]),
+}
+for _name, (_res, _args) in EXPORTED.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class NvkvLayer(ctypes.Structure):
+    """Mirror of `struct nvkv_layer` in include/nvkv.h."""
+    _fields_ = [("precision", _i), ("q", _p), ("k_data", _p), ("k_scale", _p), ("v_data", _p), ("v_scale", _p),
+                ("k_gscale", _f), ("v_gscale", _f), ("out", _p)]
+
+
+def status_string(st: int) -> str:
+    return _lib.nvkv_status_string(st).decode()
+
+
+def version() -> int:
+    return _lib.nvkv_version()
+
+
+def _check(name: str, st: int):
+    if st != 0:
+        raise RuntimeError(f"{name} failed: status {st} ({status_string(st)})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, dtype, name, cuda=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if cuda and t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------------------------------------
+# pools
+# ------------------------------------------------------------------------------------------------
+def alloc_nvfp4_pool(num_pages: int, num_kv_heads: int, device, fill: int | None = 0):
+    """NVFP4 pools of one layer: dict of k_data, k_scale, v_data, v_scale (uint8, layout in nvkv.h)."""
+    mk = (lambda n: torch.zeros((num_pages, num_kv_heads, n), dtype=torch.uint8, device=device)) if fill == 0 else \
+         (lambda n: torch.full((num_pages, num_kv_heads, n), fill, dtype=torch.uint8, device=device)) if fill is not None \
+         else (lambda n: torch.empty((num_pages, num_kv_heads, n), dtype=torch.uint8, device=device))
+    return {"k_data": mk(NVFP4_DATA_BYTES), "k_scale": mk(NVFP4_SCALE_BYTES),
+            "v_data": mk(NVFP4_DATA_BYTES), "v_scale": mk(NVFP4_SCALE_BYTES)}
+
+
+def alloc_fp8_pool(num_pages: int, num_kv_heads: int, device, fill: int | None = 0):
+    mk = (lambda: torch.full((num_pages, num_kv_heads, FP8_BYTES), fill, dtype=torch.uint8, device=device)) \
+        if fill is not None else (lambda: torch.empty((num_pages, num_kv_heads, FP8_BYTES), dtype=torch.uint8, device=device))
+    return {"k": mk(), "v": mk()}
+
+
+def nvfp4_pool_bytes(num_pages: int, num_kv_heads: int) -> int:
+    return num_pages * num_kv_heads * 2 * (NVFP4_DATA_BYTES + NVFP4_SCALE_BYTES)
+
+
+# ------------------------------------------------------------------------------------------------
+# a1: per-tensor scale
+# ------------------------------------------------------------------------------------------------
+def global_scale(x: torch.Tensor, divisor: float = NVFP4_GLOBAL_DIVISOR, in_scale: float = 1.0,
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32(max|x| / divisor) computed on the device; returns a 1-element float32 device tensor."""
+    if x.dtype == torch.bfloat16:
+        dt = IN_BF16
+    elif x.dtype == torch.uint8:
+        dt = IN_FP8
+    else:
+        raise TypeError("x must be bfloat16 or uint8 (E4M3 bytes)")
+    _need(x, x.dtype, "x")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(_lib.nvkv_global_scale_workspace_size(), dtype=torch.uint8, device=x.device)
+    _check("nvkv_global_scale", _lib.nvkv_global_scale(_ptr(x), dt, in_scale, x.numel(), divisor, _ptr(out),
+                                                       _ptr(workspace), workspace.numel(), _stream(x)))
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# a2 / a5: quantize-on-write
+# ------------------------------------------------------------------------------------------------
+def nvfp4_quantize_append(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, k_gscale: float, v_gscale: float,
+                          pool: dict, k_in_scale: float = 1.0, v_in_scale: float = 1.0):
+    """Quantize k, v ([n_tok][H_kv][128], bf16 or E4M3 bytes) into the NVFP4 pool at `slots` (int32)."""
+    dt = IN_BF16 if k.dtype == torch.bfloat16 else IN_FP8
+    _need(k, k.dtype, "k")
+    _need(v, k.dtype, "v")
+    _need(slots, torch.int32, "slots")
+    if k.dim() != 3 or k.shape != v.shape or k.shape[2] != HEAD_DIM or slots.numel() != k.shape[0]:
+        raise ValueError("k, v must be [n_tok][H_kv][128] and slots [n_tok]")
+    for key in ("k_data", "k_scale", "v_data", "v_scale"):
+        _need(pool[key], torch.uint8, key)
+    _check("nvfp4_kv_quantize_append", _lib.nvfp4_kv_quantize_append(
+        _ptr(k), _ptr(v), dt, k_in_scale, v_in_scale, _ptr(slots), k.shape[0], k.shape[1], HEAD_DIM, PAGE_SIZE,
+        k_gscale, v_gscale, _ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]), _ptr(pool["v_scale"]),
+        _stream(k)))
+
+
+def fp8_quantize_append(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, k_scale: float, v_scale: float,
+                        pool: dict):
+    _need(k, torch.bfloat16, "k")
+    _need(v, torch.bfloat16, "v")
+    _need(slots, torch.int32, "slots")
+    if k.dim() != 3 or k.shape != v.shape or k.shape[2] != HEAD_DIM or slots.numel() != k.shape[0]:
+        raise ValueError("k, v must be [n_tok][H_kv][128] and slots [n_tok]")
+    _check("fp8_kv_quantize_append", _lib.fp8_kv_quantize_append(
+        _ptr(k), _ptr(v), _ptr(slots), k.shape[0], k.shape[1], HEAD_DIM, PAGE_SIZE, k_scale, v_scale,
+        _ptr(pool["k"]), _ptr(pool["v"]), _stream(k)))
+
+
+# ------------------------------------------------------------------------------------------------
+# a3 / a4 / a5 / a7 / a8: decode
+# ------------------------------------------------------------------------------------------------
+def plan_decode(batch: int, num_kv_heads: int, max_seq_len: int, total_tokens: int = 0, force_pages_per_split: int = 0):
+    pps, ns = _i(), _i()
+    _check("nvkv_plan_decode", _lib.nvkv_plan_decode(batch, num_kv_heads, max_seq_len, total_tokens,
+                                                     force_pages_per_split, ctypes.byref(pps), ctypes.byref(ns)))
+    return pps.value, ns.value
+
+
+def decode_workspace_size(batch: int, num_q_heads: int, num_splits: int) -> int:
+    return _lib.nvkv_decode_workspace_size(batch, num_q_heads, HEAD_DIM, num_splits)
+
+
+def _decode_prep(q, page_table, seq_lens, plan, out, workspace):
+    _need(q, torch.bfloat16, "q")
+    _need(page_table, torch.int32, "page_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch][H_q][128]")
+    b, hq, _ = q.shape
+    if page_table.dim() != 2 or page_table.shape[0] != b or seq_lens.numel() != b:
+        raise ValueError("page_table must be [batch][max_pages] and seq_lens [batch]")
+    pps, ns = plan
+    if out is None:
+        out = torch.empty((b, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    need = decode_workspace_size(b, hq, ns)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return b, hq, pps, ns, out, workspace, ws_bytes
+
+
+def nvfp4_decode(q: torch.Tensor, pool: dict, k_gscale: float, v_gscale: float, page_table: torch.Tensor,
+                 seq_lens: torch.Tensor, sm_scale: float, plan, num_kv_heads: int, new_k=None, new_v=None,
+                 out=None, workspace=None) -> torch.Tensor:
+    """One decode step over an NVFP4 pool; returns out [batch][H_q][128] fp32."""
+    b, hq, pps, ns, out, workspace, ws_bytes = _decode_prep(q, page_table, seq_lens, plan, out, workspace)
+    if new_k is not None:
+        _need(new_k, torch.bfloat16, "new_k")
+        _need(new_v, torch.bfloat16, "new_v")
+    _check("nvfp4_paged_decode_attn", _lib.nvfp4_paged_decode_attn(
+        _ptr(q), _ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]), _ptr(pool["v_scale"]),
+        k_gscale, v_gscale, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), b, hq, num_kv_heads, HEAD_DIM,
+        PAGE_SIZE, sm_scale, pps, ns, _ptr(new_k), _ptr(new_v), _ptr(out), _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def fp8_decode(q: torch.Tensor, pool: dict, k_scale: float, v_scale: float, page_table: torch.Tensor,
+               seq_lens: torch.Tensor, sm_scale: float, plan, num_kv_heads: int, out=None, workspace=None):
+    b, hq, pps, ns, out, workspace, ws_bytes = _decode_prep(q, page_table, seq_lens, plan, out, workspace)
+    _check("fp8_paged_decode_attn", _lib.fp8_paged_decode_attn(
+        _ptr(q), _ptr(pool["k"]), _ptr(pool["v"]), k_scale, v_scale, _ptr(page_table), page_table.shape[1],
+        _ptr(seq_lens), b, hq, num_kv_heads, HEAD_DIM, PAGE_SIZE, sm_scale, pps, ns, _ptr(out), _ptr(workspace),
+        ws_bytes, _stream(q)))
+    return out
+
+
+def decode_layers(layers: list, page_table: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float, plan,
+                  num_kv_heads: int, workspace=None):
+    """One decode step across layers.  Each entry: dict(precision, q, pool, k_gscale, v_gscale, out)."""
+    if not layers:
+        raise ValueError("no layers")
+    q0 = layers[0]["q"]
+    b, hq, pps, ns, _, workspace, ws_bytes = _decode_prep(q0, page_table, seq_lens, plan, layers[0]["out"], workspace)
+    arr = (NvkvLayer * len(layers))()
+    for i, L in enumerate(layers):
+        _need(L["q"], torch.bfloat16, "q")
+        _need(L["out"], torch.float32, "out")
+        if L["q"].shape != q0.shape or L["out"].shape != q0.shape:
+            raise ValueError("all layers must share q / out shapes")
+        pool = L["pool"]
+        if L["precision"] == PREC_NVFP4:
+            arr[i] = NvkvLayer(PREC_NVFP4, L["q"].data_ptr(), pool["k_data"].data_ptr(), pool["k_scale"].data_ptr(),
+                               pool["v_data"].data_ptr(), pool["v_scale"].data_ptr(), L["k_gscale"], L["v_gscale"],
+                               L["out"].data_ptr())
+        else:
+            arr[i] = NvkvLayer(PREC_FP8, L["q"].data_ptr(), pool["k"].data_ptr(), None, pool["v"].data_ptr(), None,
+                               L["k_gscale"], L["v_gscale"], L["out"].data_ptr())
+    _check("nvkv_decode_layers", _lib.nvkv_decode_layers(
+        ctypes.cast(arr, ctypes.c_void_p), len(layers), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), b, hq,
+        num_kv_heads, HEAD_DIM, PAGE_SIZE, sm_scale, pps, ns, _ptr(workspace), ws_bytes, _stream(q0)))
+    return [L["out"] for L in layers]
+
+
+# ------------------------------------------------------------------------------------------------
+# a6: prefix -> FP8 workspace
+# ------------------------------------------------------------------------------------------------
+def dequant_to_workspace(pool: dict, k_gscale: float, v_gscale: float, page_table: torch.Tensor,
+                         prefix_lens: torch.Tensor, ws_offsets: torch.Tensor, max_prefix_len: int,
+                         k_ws_scale: float, v_ws_scale: float, num_kv_heads: int, k_ws=None, v_ws=None):
+    _need(page_table, torch.int32, "page_table")
+    _need(prefix_lens, torch.int32, "prefix_lens")
+    _need(ws_offsets, torch.int32, "ws_offsets")
+    b = prefix_lens.numel()
+    if ws_offsets.numel() != b + 1:
+        raise ValueError("ws_offsets must have batch + 1 entries")
+    if k_ws is None or v_ws is None:
+        raise ValueError("k_ws and v_ws ([rows][H_kv][128] uint8) must be given")
+    _need(k_ws, torch.uint8, "k_ws")
+    _need(v_ws, torch.uint8, "v_ws")
+    _check("nvfp4_dequant_to_workspace", _lib.nvfp4_dequant_to_workspace(
+        _ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]), _ptr(pool["v_scale"]), k_gscale, v_gscale,
+        _ptr(page_table), page_table.shape[1], _ptr(prefix_lens), _ptr(ws_offsets), b, num_kv_heads, HEAD_DIM,
+        PAGE_SIZE, max_prefix_len, k_ws_scale, v_ws_scale, _ptr(k_ws), _ptr(v_ws), _stream(k_ws)))
+    return k_ws, v_ws
+
+
+def default_sm_scale() -> float:
+    return 1.0 / math.sqrt(HEAD_DIM)

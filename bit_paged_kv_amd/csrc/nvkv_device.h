@@ -1,0 +1,127 @@
+// Device-side helpers shared by the libnvkv kernels (gfx950 / CDNA4 only).
+//
+// Format (SGLang x Qwen x NVIDIA NVFP4 KV-cache story, "The Core of the Ledger" paragraphs 1-2;
+// SOAR Notes 05, "02 NVFP4 KV Cache"): 4-bit E2M1 codes two per byte, one OCP E4M3 scale per 16
+// channels, one fp32 scale per tensor; dequantized value = e2m1 * e4m3 * g.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvkv {
+
+constexpr int kHeadDim = 128;
+constexpr int kPageSize = 16;
+constexpr int kNvfp4DataBytes = 1024;   // one (page, head) block of packed E2M1 codes
+constexpr int kNvfp4ScaleBytes = 128;   // one (page, head) block of E4M3 block scales
+constexpr int kFp8Bytes = 2048;         // one (page, head) block of FP8 values
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------------------------
+// Encoders (quantize-on-write).  Round to nearest, ties to the even mantissa, saturating to the
+// largest finite magnitude; computed with exact power-of-two scalings and v_rndne_f32.
+// ---------------------------------------------------------------------------------------------
+
+// OCP E4M3 (bias 7, max 448, subnormal step 2^-9) byte of x, sign copied from x.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a < 448.0f)) return sign | 0x7Eu;            // saturate (448 and above)
+  if (a < 0.015625f) {                               // below 2^-6: subnormal grid, step 2^-9
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8; 8 is the smallest normal 0x08
+  }
+  const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // -6 .. 8
+  const uint32_t m = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - e));   // 8 .. 16
+  uint32_t code = ((uint32_t)(e + 7) << 3) + (m - 8u);   // m == 16 carries into the next binade
+  code = code > 0x7Eu ? 0x7Eu : code;
+  return sign | code;
+}
+
+// Value of a non-negative E4M3 byte (0x00..0x7E) as fp32, exactly.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+  return e == 0 ? __builtin_ldexpf((float)m, -9) : __builtin_ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// 3-bit E2M1 magnitude code of |y| (grid 0, .5, 1, 1.5 | 2, 3 | 4, 6), saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_encode_mag(float a) {
+  if (a < 2.0f) return (uint32_t)__builtin_rintf(a * 2.0f);          // 0..4 (4 = value 2)
+  if (a < 4.0f) return (uint32_t)__builtin_rintf(a) + 2u;            // 2,3,4 -> codes 4,5,6
+  if (a < 6.0f) return (uint32_t)__builtin_rintf(a * 0.5f) + 4u;     // 2,3 -> codes 6,7
+  return 7u;
+}
+
+// Block scale of a 16-value block with absolute maximum `amax`: returns the E4M3 byte and the
+// fp32 divisor fp32(s * g) of its elements (0 when the scale rounds to zero).
+__device__ __forceinline__ uint32_t nvfp4_block_scale(float amax, float g, float* den) {
+  const float six_g = 6.0f * g;
+  const float u = amax / six_g;                    // correctly rounded fp32 division
+  const uint32_t sc = e4m3_encode(u);              // u >= 0: sign bit clear
+  *den = e4m3_value(sc) * g;
+  return sc;
+}
+
+// 4-bit code of one value given its block's divisor (sign in bit 3; signed zero when den == 0).
+__device__ __forceinline__ uint32_t nvfp4_code(float x, float den) {
+  const uint32_t sgn = (__float_as_uint(x) >> 28) & 8u;
+  return sgn | (den == 0.0f ? 0u : e2m1_encode_mag(fabsf(x / den)));
+}
+
+// Quantize 16 fp32 values of one block.  Returns the E4M3 scale byte; codes[i] gets the 4-bit
+// E2M1 code (sign in bit 3).  g is the tensor's global scale (> 0).
+__device__ __forceinline__ uint32_t nvfp4_quantize_block(const float (&x)[16], float g, uint32_t (&codes)[16]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
+  float den;
+  const uint32_t sc = nvfp4_block_scale(a, g, &den);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) codes[i] = nvfp4_code(x[i], den);
+  return sc;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Input loaders
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// 8 bf16 values packed in a uint4 -> fp32 (exact)
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// gfx950 hardware converts used by the decode kernels.  With a scale operand of 1.0 they are exact
+// decodes (checked exhaustively on the device): an E2M1 pair (one byte, low nibble first) or an
+// E4M3 pair (one 16-bit half of a dword, low byte first) to two fp16 values.
+// ---------------------------------------------------------------------------------------------
+template <int BYTE>
+__device__ __forceinline__ h2 fp4x2_to_h2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, BYTE);
+}
+template <bool HIGH>
+__device__ __forceinline__ h2 fp8x2_to_h2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HIGH);
+}
+
+__device__ __forceinline__ h8 cat4(h2 a, h2 b, h2 c, h2 d) {
+  return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Wave-wide (64 lanes) butterfly reductions over the lanes that differ in the given xor bits.
+__device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+}  // namespace nvkv

@@ -1,0 +1,53 @@
+// Internal launchers behind the C ABI (arguments already validated by nvkv_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace nvkv {
+
+size_t global_scale_workspace_bytes();
+hipError_t launch_global_scale(const void* x, int in_dtype, float in_scale, size_t n, float divisor, float* out,
+                               void* workspace, hipStream_t stream);
+hipError_t launch_nvfp4_quantize(const void* k_in, const void* v_in, int in_dtype, float k_in_scale, float v_in_scale,
+                                 const int32_t* slots, int n_tok, int hkv, float gk, float gv, uint8_t* k_data,
+                                 uint8_t* k_scale, uint8_t* v_data, uint8_t* v_scale, hipStream_t stream);
+hipError_t launch_fp8_quantize(const void* k_in, const void* v_in, const int32_t* slots, int n_tok, int hkv, float sk,
+                               float sv, uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream);
+hipError_t launch_dequant_to_ws(const uint8_t* k_data, const uint8_t* k_scale, const uint8_t* v_data,
+                                const uint8_t* v_scale, float gk, float gv, const int32_t* page_table, int max_pages,
+                                const int32_t* prefix_lens, const int32_t* ws_offsets, int batch, int hkv,
+                                int max_prefix, float sk_ws, float sv_ws, uint8_t* k_ws, uint8_t* v_ws,
+                                hipStream_t stream);
+
+// Decode: one wavefront per (sequence, kv head, split); partial softmax states are merged by a
+// second kernel when num_splits > 1.
+enum CacheFormat { kFmtNvfp4 = 0, kFmtFp8 = 1 };
+
+struct DecodeArgs {
+  int format;                 // CacheFormat
+  const void* q;              // bf16 [B][Hq][128]
+  const uint8_t* k_data;
+  const uint8_t* k_scale;     // NVFP4 only
+  const uint8_t* v_data;
+  const uint8_t* v_scale;     // NVFP4 only
+  float k_gscale, v_gscale;   // NVFP4 global scales, or FP8 per-tensor scales
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* seq_lens;
+  int batch, hq, hkv;
+  float sm_scale;
+  int pages_per_split, num_splits;
+  const void* new_k;          // NVFP4 fused append, or null
+  const void* new_v;
+  float* out;                 // fp32 [B][Hq][128]
+  void* workspace;            // partials when num_splits > 1
+};
+
+size_t decode_workspace_bytes(int batch, int hq, int num_splits);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace nvkv

@@ -1,0 +1,219 @@
+"""GPU parity of decode attention through the C ABI against the fp64 oracle on the oracle's own
+dequantized cache: max-abs <= 2e-3 and rel-L2 <= 1e-3 over the whole output (tests/helpers.py)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attention as o_att
+from oracle import fp8 as o_fp8
+from oracle import nvfp4 as o_nv
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import bit_paged_kv_amd as nv
+    return nv
+
+
+def _run_nvfp4(nv, wl, pool, gk, gv, force_pps=0, layer=0, fused=False):
+    pt, sl = H.gpu_tables(wl, DEV)
+    plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), int(wl.total_lens.sum()), force_pps)
+    q = wl.q(layer).to(DEV)
+    nk = wl.new_token("k", layer).to(DEV) if fused else None
+    nvv = wl.new_token("v", layer).to(DEV) if fused else None
+    out = nv.nvfp4_decode(q, pool, gk, gv, pt, sl, wl.sm_scale, plan, wl.h_kv, new_k=nk, new_v=nvv)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), plan
+
+
+def test_decode_tiny(nv):
+    wl = workloads.config(0)
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    want = H.oracle_nvfp4_decode(wl, wl.q().float().numpy(), ks, vs, gk, gv)
+    pool, _, _ = H.gpu_nvfp4_layer(wl, 0, DEV, fill=0xFF)   # unused bytes hold NaN scale patterns
+    for pps in (0, 2, 4, 16):
+        got, plan = _run_nvfp4(nv, wl, pool, gk, gv, force_pps=pps)
+        H.assert_attention_close(got, want, f"tiny plan={plan}")
+
+
+@pytest.fixture(scope="module")
+def ragged(nv):
+    wl = workloads.Workload(name="ragged-small", seed=21, batch=7, h_kv=2, h_q=16,
+                            seq_lens=[1, 15, 16, 17, 33, 700, 1283], extra_pages=5)
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    want = H.oracle_nvfp4_decode(wl, wl.q().float().numpy(), ks, vs, gk, gv)
+    pool, _, _ = H.gpu_nvfp4_layer(wl, 0, DEV, fill=0xFF)
+    return wl, pool, gk, gv, want
+
+
+@pytest.mark.parametrize("pps", [0, 2, 4, 6, 32, 1000])
+def test_decode_ragged_split_sizes(nv, ragged, pps):
+    wl, pool, gk, gv, want = ragged
+    got, plan = _run_nvfp4(nv, wl, pool, float(gk), float(gv), force_pps=pps)
+    H.assert_attention_close(got, want, f"ragged plan={plan}")
+
+
+def test_decode_split_count_invariance(nv, ragged):
+    wl, pool, gk, gv, _ = ragged
+    outs = [_run_nvfp4(nv, wl, pool, float(gk), float(gv), force_pps=p)[0] for p in (2, 8, 1000)]
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() < 1e-5
+
+
+@pytest.mark.parametrize("group", [1, 2, 8, 16])
+def test_decode_gqa_groups(nv, group):
+    wl = workloads.Workload(name=f"gqa{group}", seed=30 + group, batch=2, h_kv=2, h_q=2 * group,
+                            seq_lens=[257, 100])
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    want = H.oracle_nvfp4_decode(wl, wl.q().float().numpy(), ks, vs, gk, gv)
+    pool, _, _ = H.gpu_nvfp4_layer(wl, 0, DEV)
+    got, plan = _run_nvfp4(nv, wl, pool, float(gk), float(gv))
+    H.assert_attention_close(got, want, f"group {group}")
+
+
+def test_decode_page_permutation_invariance(nv):
+    a = workloads.Workload(name="perm", seed=40, batch=2, h_kv=2, h_q=8, seq_lens=[500, 231], page_mode="identity")
+    b = workloads.Workload(name="perm", seed=40, batch=2, h_kv=2, h_q=8, seq_lens=[500, 231], extra_pages=11)
+    assert not np.array_equal(a.page_table, b.page_table[:, :a.page_table.shape[1]])
+    outs = []
+    for wl in (a, b):
+        pool, gk, gv = H.gpu_nvfp4_layer(wl, 0, DEV)
+        outs.append(_run_nvfp4(nv, wl, pool, gk, gv, force_pps=4)[0])
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_decode_fused_append(nv):
+    wl = workloads.Workload(name="append", seed=50, batch=6, h_kv=2, h_q=16,
+                            seq_lens=[15, 16, 31, 1, 200, 513], append=True, extra_pages=3)
+    ks, vs = H.oracle_inputs(wl)                        # cache + new token
+    gk, gv = H.oracle_nvfp4_scales(wl)                  # from the cache only
+    want = H.oracle_nvfp4_decode(wl, wl.q().float().numpy(), ks, vs, gk, gv)
+    want_pool = H.oracle_nvfp4_pool(wl, ks, vs, gk, gv, fill=0x3C)
+    for pps in (0, 2, 1000):
+        pool, g_k, g_v = H.gpu_nvfp4_layer(wl, 0, DEV, fill=0x3C)   # cache without the new tokens
+        assert (np.float32(g_k), np.float32(g_v)) == (gk, gv)
+        got, plan = _run_nvfp4(nv, wl, pool, g_k, g_v, force_pps=pps, fused=True)
+        H.assert_attention_close(got, want, f"fused append plan={plan}")
+        for key in ("k_data", "k_scale", "v_data", "v_scale"):
+            assert np.array_equal(pool[key].cpu().numpy(), want_pool[key]), key
+
+
+def _fp8_case(wl, layer=0):
+    ks, vs = H.oracle_inputs(wl, layer)
+    sk = o_fp8.fp8_scale(np.concatenate(ks))
+    sv = o_fp8.fp8_scale(np.concatenate(vs))
+    want = H.oracle_fp8_decode(wl, wl.q(layer).float().numpy(), ks, vs, sk, sv)
+    return want, sk, sv
+
+
+def test_fp8_decode(nv):
+    from bit_paged_kv_amd import paged
+    wl = workloads.Workload(name="fp8", seed=60, batch=4, h_kv=2, h_q=8, seq_lens=[1, 17, 300, 1029],
+                            chan="outlier2", extra_pages=2)
+    want, sk, sv = _fp8_case(wl)
+    k, v, slots = H.gpu_all_tokens(wl, 0, DEV)
+    pool, g_sk, g_sv = paged.build_fp8_cache(k, v, slots, wl.num_pages, fill=0xFF)
+    pt, sl = H.gpu_tables(wl, DEV)
+    for pps in (0, 2, 64):
+        plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), 0, pps)
+        got = nv.fp8_decode(wl.q().to(DEV), pool, g_sk, g_sv, pt, sl, wl.sm_scale, plan, wl.h_kv)
+        H.assert_attention_close(got.cpu().numpy(), want, f"fp8 plan={plan}")
+
+
+def test_decode_layers_mixed_stack(nv):
+    from bit_paged_kv_amd import paged
+    wl = workloads.Workload(name="mixed-small", seed=70, batch=3, h_kv=2, h_q=8, seq_lens=[64, 300, 17],
+                            chan="outlier2", layers=4, fp8_layers=(0, 3))
+    pt, sl = H.gpu_tables(wl, DEV)
+    plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()))
+    layers, wants = [], []
+    for layer in range(wl.layers):
+        k, v, slots = H.gpu_all_tokens(wl, layer, DEV)
+        if wl.is_fp8(layer):
+            pool, s1, s2 = paged.build_fp8_cache(k, v, slots, wl.num_pages)
+            want, _, _ = _fp8_case(wl, layer)
+            prec = nv.PREC_FP8
+        else:
+            pool, s1, s2 = paged.build_nvfp4_cache(k, v, slots, wl.num_pages)
+            ks, vs = H.oracle_inputs(wl, layer)
+            gk, gv = H.oracle_nvfp4_scales(wl, layer)
+            want = H.oracle_nvfp4_decode(wl, wl.q(layer).float().numpy(), ks, vs, gk, gv)
+            prec = nv.PREC_NVFP4
+        layers.append(dict(precision=prec, q=wl.q(layer).to(DEV), pool=pool, k_gscale=s1, v_gscale=s2,
+                           out=torch.empty((wl.batch, wl.h_q, 128), dtype=torch.float32, device=DEV)))
+        wants.append(want)
+    outs = nv.decode_layers(layers, pt, sl, wl.sm_scale, plan, wl.h_kv)
+    torch.cuda.synchronize()
+    for i, (o, w) in enumerate(zip(outs, wants)):
+        H.assert_attention_close(o.cpu().numpy(), w, f"layer {i}")
+
+
+def _sampled_full_size(nv, index, samples):
+    """Full-size workload in the bench's launch configuration; the oracle recomputes the sampled
+    (sequence, kv head) rows from the same seeded inputs (never from anything the GPU produced)."""
+    wl = workloads.config(index)
+    ks = [wl.kv("k", b) for b in range(wl.batch)]
+    vs = [wl.kv("v", b) for b in range(wl.batch)]
+    print(f"cfg{index}: inputs generated", flush=True)
+    from bit_paged_kv_amd import paged
+    slots = torch.from_numpy(np.concatenate([wl.slots(b) for b in range(wl.batch)])).to(DEV)
+    k_all = torch.cat(ks).to(DEV)
+    v_all = torch.cat(vs).to(DEV)
+    pool, gk, gv = paged.build_nvfp4_cache(k_all, v_all, slots, wl.num_pages)
+    del k_all, v_all
+    pt, sl = H.gpu_tables(wl, DEV)
+    plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), int(wl.total_lens.sum()))
+    q = wl.q()
+    fused = wl.append
+    nk = wl.new_token("k") if fused else None
+    nvv = wl.new_token("v") if fused else None
+    out = nv.nvfp4_decode(q.to(DEV), pool, gk, gv, pt, sl, wl.sm_scale, plan, wl.h_kv,
+                          new_k=nk.to(DEV) if fused else None, new_v=nvv.to(DEV) if fused else None).cpu().numpy()
+    del pool
+    torch.cuda.empty_cache()
+    print(f"cfg{index}: GPU step done, plan {plan}", flush=True)
+    # the oracle's own global scales, over the whole cached tensors
+    ogk = o_nv.global_scale(np.array([max(float(t.float().abs().max()) for t in ks)], np.float32))
+    ogv = o_nv.global_scale(np.array([max(float(t.float().abs().max()) for t in vs)], np.float32))
+    assert (np.float32(gk), np.float32(gv)) == (ogk, ogv)
+    qf = q.float().numpy()
+    G = wl.group
+    for b, hk in samples:
+        k = ks[b][:, hk].float().numpy()
+        v = vs[b][:, hk].float().numpy()
+        if fused:
+            k = np.concatenate([k, nk[b, hk][None].float().numpy()])
+            v = np.concatenate([v, nvv[b, hk][None].float().numpy()])
+        ck, sk = o_nv.quantize_blocks(k, ogk)
+        cv, sv = o_nv.quantize_blocks(v, ogv)
+        kh = o_nv.dequantize_blocks(ck, sk, ogk)[:, None]
+        vh = o_nv.dequantize_blocks(cv, sv, ogv)[:, None]
+        want = o_att.decode_attention_one(qf[b, hk * G:(hk + 1) * G], kh, vh, wl.sm_scale)
+        err = H.assert_attention_close(out[b, hk * G:(hk + 1) * G], want, f"cfg{index} b={b} hk={hk} plan={plan}")
+        print(f"cfg{index}: sample b={b} hk={hk} max-abs {err[0]:.2e} rel-L2 {err[1]:.2e}", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_long_sampled(nv):
+    _sampled_full_size(nv, 2, [(0, 0), (3, 7)])
+
+
+@pytest.mark.timeout(600)
+def test_full_size_batch32_sampled(nv):
+    _sampled_full_size(nv, 1, [(0, 0), (17, 3), (31, 7)])
+
+
+@pytest.mark.timeout(600)
+def test_full_size_ragged_fused_sampled(nv):
+    wl = workloads.config(3)
+    longest = int(np.argmax(wl.seq_lens))
+    shortest = int(np.argmin(wl.seq_lens))
+    _sampled_full_size(nv, 3, [(longest, 2), (shortest, 5)])

@@ -1,0 +1,193 @@
+"""GPU parity of the write side through the C ABI: bytes and scales must equal the oracle's bit for bit."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import codecs as o_codecs
+from oracle import fp8 as o_fp8
+from oracle import layout as o_layout
+from oracle import nvfp4 as o_nv
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import bit_paged_kv_amd as nv
+    return nv
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("n", [1, 7, 16, 4093, 1 << 20])
+def test_global_scale_bf16_bitexact(nv, n):
+    rng = np.random.default_rng(n)
+    x = _bf16(rng.standard_normal(n) * np.exp(rng.uniform(-3, 3, n)))
+    if n > 4:
+        x[n - 1] = -1000.0  # the maximum sits in the tail
+    want = o_nv.global_scale(x.float().numpy())
+    got = nv.global_scale(x.to(DEV)).item()
+    assert np.float32(got) == want
+    want8 = o_fp8.fp8_scale(x.float().numpy())
+    got8 = nv.global_scale(x.to(DEV), divisor=448.0).item()
+    assert np.float32(got8) == want8
+
+
+def test_global_scale_fp8_input_bitexact(nv):
+    rng = np.random.default_rng(3)
+    b = rng.integers(0, 256, 10001).astype(np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x11         # no NaN patterns
+    s_in = np.float32(0.37)
+    x = (o_codecs.e4m3_decode(b).astype(np.float32) * s_in).astype(np.float32)
+    want = o_nv.global_scale(x)
+    got = nv.global_scale(torch.from_numpy(b).to(DEV), in_scale=float(s_in)).item()
+    assert np.float32(got) == want
+
+
+def _check_pool(got, want):
+    for key in ("k_data", "k_scale", "v_data", "v_scale"):
+        g = got[key].cpu().numpy()
+        bad = np.argwhere(g != want[key])
+        assert bad.size == 0, f"{key}: {len(bad)} bytes differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("fill", [0, 0xA5])
+def test_nvfp4_quantize_tiny_bitexact(nv, fill):
+    wl = workloads.config(0)
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    want = H.oracle_nvfp4_pool(wl, ks, vs, gk, gv, fill=fill)
+    pool, g_k, g_v = H.gpu_nvfp4_layer(wl, 0, DEV, fill=fill)
+    assert (np.float32(g_k), np.float32(g_v)) == (gk, gv)
+    _check_pool(pool, want)
+
+
+def test_nvfp4_quantize_ragged_scattered_bitexact(nv):
+    # several sequences, partial last pages, permuted pool with spare pages: consecutive tokens share
+    # V-data bytes and are written by different threads of one launch
+    wl = workloads.Workload(name="ragged-small", seed=77, batch=5, h_kv=3, h_q=6,
+                            seq_lens=[1, 17, 300, 64, 95], extra_pages=7)
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    want = H.oracle_nvfp4_pool(wl, ks, vs, gk, gv, fill=0x5C)
+    pool, _, _ = H.gpu_nvfp4_layer(wl, 0, DEV, fill=0x5C)
+    _check_pool(pool, want)
+
+
+def test_nvfp4_quantize_golden_and_edge_blocks_bitexact(nv):
+    """The hand-worked blocks, plus ties, saturation, subnormal and zero scales, signed zeros."""
+    gold = json.load(open(os.path.join(GOLD, "nvfp4_worked_blocks.json")))["blocks"]
+    rng = np.random.default_rng(5)
+    g = np.float32(2.0 ** -8)
+    rows = []
+    for blk in gold:
+        if np.float32(blk["g"]) == g:
+            rows.append(np.array(blk["x"], dtype=np.float32))
+    grid = np.array([0, .25, .5, .75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 7], dtype=np.float32)
+    for s in (1.0, 1.75, 448.0, 2.0 ** -9, 3 * 2.0 ** -9, 0.0):
+        rows.append(np.float32(grid * s * float(g)) * np.where(rng.random(16) < 0.5, -1, 1).astype(np.float32))
+    rows.append(np.array([-0.0] * 8 + [0.0] * 8, dtype=np.float32))
+    rows.append(np.float32(rng.standard_normal(16) * 1e4))            # far above 448 * 6 * g: saturates
+    rows.append(np.float32(rng.standard_normal(16) * 1e-7))           # scale rounds to zero
+    blocks = np.stack(rows)
+    # round to bf16 (the input type) and keep those rows; 8 blocks make one token of one head
+    xb = _bf16(blocks).float().numpy()
+    n_tok = (xb.shape[0] + 7) // 8
+    tok = np.zeros((n_tok * 8, 16), dtype=np.float32)
+    tok[:xb.shape[0]] = xb
+    tok = tok.reshape(n_tok, 1, 128)
+    slots = np.arange(n_tok, dtype=np.int32) * 3 % (16 * 4)               # scattered in 4 pages
+    dshape, sshape = o_layout.nvfp4_pool_shapes(4, 1)
+    want = {k: np.zeros(s, np.uint8) for k, s in (("k_data", dshape), ("k_scale", sshape),
+                                                  ("v_data", dshape), ("v_scale", sshape))}
+    c, s = o_nv.quantize_blocks(tok, g)
+    o_layout.write_nvfp4_tokens(want["k_data"], want["k_scale"], "k", slots, c, s)
+    o_layout.write_nvfp4_tokens(want["v_data"], want["v_scale"], "v", slots, c, s)
+    pool = nv.alloc_nvfp4_pool(4, 1, DEV)
+    t = _bf16(tok).to(DEV)
+    nv.nvfp4_quantize_append(t, t.clone(), torch.from_numpy(slots).to(DEV), float(g), float(g), pool)
+    _check_pool(pool, want)
+    # the hand-worked codes survive the GPU round trip too
+    codes, _ = o_layout.read_nvfp4_tokens(pool["k_data"].cpu().numpy(), pool["k_scale"].cpu().numpy(), "k", slots)
+    flat = codes.reshape(-1, 16)
+    for i, blk in enumerate(b for b in gold if np.float32(b["g"]) == g):
+        assert flat[i].tolist() == blk["codes"], blk["name"]
+
+
+def test_nvfp4_quantize_fp8_input_bitexact(nv):
+    rng = np.random.default_rng(9)
+    n_tok, h = 40, 2
+    b = rng.integers(0, 256, (n_tok, h, 128)).astype(np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x33
+    sk, sv = np.float32(0.013), np.float32(3.5)
+    xk = (o_codecs.e4m3_decode(b).astype(np.float32) * sk).astype(np.float32)
+    xv = (o_codecs.e4m3_decode(b[::-1].copy()).astype(np.float32) * sv).astype(np.float32)
+    gk, gv = o_nv.global_scale(xk), o_nv.global_scale(xv)
+    slots = rng.permutation(64)[:n_tok].astype(np.int32)
+    dshape, sshape = o_layout.nvfp4_pool_shapes(4, h)
+    want = {k: np.zeros(s, np.uint8) for k, s in (("k_data", dshape), ("k_scale", sshape),
+                                                  ("v_data", dshape), ("v_scale", sshape))}
+    ck, csk = o_nv.quantize_blocks(xk, gk)
+    cv, csv = o_nv.quantize_blocks(xv, gv)
+    o_layout.write_nvfp4_tokens(want["k_data"], want["k_scale"], "k", slots, ck, csk)
+    o_layout.write_nvfp4_tokens(want["v_data"], want["v_scale"], "v", slots, cv, csv)
+    pool = nv.alloc_nvfp4_pool(4, h, DEV)
+    gk_gpu = nv.global_scale(torch.from_numpy(b).to(DEV), in_scale=float(sk)).item()
+    assert np.float32(gk_gpu) == gk
+    nv.nvfp4_quantize_append(torch.from_numpy(b).to(DEV), torch.from_numpy(b[::-1].copy()).to(DEV),
+                             torch.from_numpy(slots).to(DEV), float(gk), float(gv), pool,
+                             k_in_scale=float(sk), v_in_scale=float(sv))
+    _check_pool(pool, want)
+
+
+def test_fp8_quantize_bitexact(nv):
+    wl = workloads.Workload(name="fp8-small", seed=11, batch=3, h_kv=2, h_q=8, seq_lens=[33, 5, 70], extra_pages=3)
+    ks, vs = H.oracle_inputs(wl)
+    sk = o_fp8.fp8_scale(np.concatenate(ks))
+    sv = o_fp8.fp8_scale(np.concatenate(vs))
+    want_k = np.full(o_layout.fp8_pool_shape(wl.num_pages, wl.h_kv), 0x7F, np.uint8)
+    want_v = want_k.copy()
+    for b in range(wl.batch):
+        o_layout.write_fp8_tokens(want_k, "k", wl.slots(b), o_fp8.fp8_quantize(ks[b], sk))
+        o_layout.write_fp8_tokens(want_v, "v", wl.slots(b), o_fp8.fp8_quantize(vs[b], sv))
+    from bit_paged_kv_amd import paged
+    k, v, slots = H.gpu_all_tokens(wl, 0, DEV)
+    pool, g_sk, g_sv = paged.build_fp8_cache(k, v, slots, wl.num_pages, fill=0x7F)
+    assert (np.float32(g_sk), np.float32(g_sv)) == (sk, sv)
+    assert np.array_equal(pool["k"].cpu().numpy(), want_k)
+    assert np.array_equal(pool["v"].cpu().numpy(), want_v)
+
+
+def test_dequant_to_workspace_bitexact(nv):
+    wl = workloads.Workload(name="ws-small", seed=13, batch=3, h_kv=2, h_q=4, seq_lens=[50, 16, 129])
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    s_wk, s_wv = np.float32(6.0) * gk, np.float32(6.0) * gv    # the layer's FP8 scale, amax / 448
+    prefix = np.array([37, 16, 129], dtype=np.int32)
+    offs = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int32) + np.array([0, 5, 5, 5], dtype=np.int32)
+    rows = int(offs[-1]) + 3
+    want_k = np.full((rows, wl.h_kv, 128), 0xEE, np.uint8)
+    want_v = want_k.copy()
+    for b in range(wl.batch):
+        n = prefix[b]
+        ck, sck = o_nv.quantize_blocks(ks[b][:n], gk)
+        cv, scv = o_nv.quantize_blocks(vs[b][:n], gv)
+        want_k[offs[b]:offs[b] + n] = o_fp8.nvfp4_to_fp8_workspace(ck, sck, gk, s_wk)
+        want_v[offs[b]:offs[b] + n] = o_fp8.nvfp4_to_fp8_workspace(cv, scv, gv, s_wv)
+    pool, _, _ = H.gpu_nvfp4_layer(wl, 0, DEV)
+    kw = torch.full((rows, wl.h_kv, 128), 0xEE, dtype=torch.uint8, device=DEV)
+    vw = kw.clone()
+    nv.dequant_to_workspace(pool, float(gk), float(gv), torch.from_numpy(wl.page_table).to(DEV),
+                            torch.from_numpy(prefix).to(DEV), torch.from_numpy(offs).to(DEV), int(prefix.max()),
+                            float(s_wk), float(s_wv), wl.h_kv, kw, vw)
+    assert np.array_equal(kw.cpu().numpy(), want_k)
+    assert np.array_equal(vw.cpu().numpy(), want_v)
