@@ -55,12 +55,13 @@ def e2m1_decode(codes) -> np.ndarray:
     return E2M1_TABLE[np.asarray(codes, dtype=np.uint8) & 0xF]
 
 
-def e2m1_encode_magnitude(abs_y, chunk: int = 1 << 22) -> np.ndarray:
+def e2m1_encode_magnitude(abs_y) -> np.ndarray:
     """3-bit magnitude code of |y|: nearest E2M1 magnitude, ties to even mantissa, saturating at 6.
 
-    ``abs_y`` holds non-negative fp32 values (it is widened to fp64, which is
-    exact, so the distances below are exact).  Values above 6 -- including
-    +inf -- saturate to code 7 (= 6).  NaN is outside the contract and raises.
+    ``abs_y`` holds non-negative fp32 values (widened to fp64, which is exact, so the distances
+    below are exact).  The two grid points that bracket each value are found by binary search;
+    the nearer one wins and a tie goes to the one with mantissa bit 0 (even code).  Values above 6
+    -- including +inf -- saturate to code 7 (= 6).  NaN is outside the contract and raises.
     """
     a = np.asarray(abs_y, dtype=np.float32).astype(np.float64)
     if np.isnan(a).any():
@@ -69,22 +70,25 @@ def e2m1_encode_magnitude(abs_y, chunk: int = 1 << 22) -> np.ndarray:
         raise ValueError("E2M1 encode expects magnitudes")
     flat = a.reshape(-1)
     out = np.empty(flat.shape, dtype=np.uint8)
-    grid = E2M1_MAGNITUDES
-    for s in range(0, flat.size, chunk):
-        v = flat[s:s + chunk]
-        big = v > grid[-1]
-        vv = np.where(big, grid[-1], v)
-        dist = np.abs(vv[:, None] - grid[None, :])          # exact in fp64
-        best = dist.min(axis=1, keepdims=True)
-        is_best = dist == best
-        # among equally near grid points prefer the even mantissa (code LSB 0)
-        even = (np.arange(8) & 1) == 0
-        pick_even = is_best & even[None, :]
-        has_even = pick_even.any(axis=1)
-        code = np.where(has_even, np.argmax(pick_even, axis=1), np.argmax(is_best, axis=1))
-        code = np.where(big, 7, code)
-        out[s:s + chunk] = code.astype(np.uint8)
+    for s in range(0, flat.size, _CHUNK):
+        out[s:s + _CHUNK] = _nearest_even(E2M1_MAGNITUDES, flat[s:s + _CHUNK])
     return out.reshape(a.shape)
+
+
+_CHUNK = 1 << 20   # elements per piece (keeps temporaries small; results do not depend on it)
+
+
+def _nearest_even(grid: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Index of the grid point nearest to each v >= 0 (fp64, exact distances); a tie goes to the
+    even index (mantissa bit 0); values at or above the last point map to it (saturation)."""
+    big = v >= grid[-1]
+    hi = np.clip(np.searchsorted(grid, v, side="left"), 1, grid.size - 1)   # grid[hi-1] < v <= grid[hi]
+    lo = hi - 1
+    d_lo = v - grid[lo]
+    d_hi = grid[hi] - v
+    code = np.where(d_lo < d_hi, lo, hi)
+    code = np.where(d_lo == d_hi, np.where((lo & 1) == 0, lo, hi), code)
+    return np.where(big, grid.size - 1, code).astype(np.uint8)
 
 
 def _e4m3_value(byte: int) -> float:
@@ -121,17 +125,10 @@ def e4m3_encode(x) -> np.ndarray:
     x32 = np.asarray(x, dtype=np.float32)
     if np.isnan(x32).any():
         raise ValueError("E4M3 encode: NaN input is outside the contract")
-    sign = np.signbit(x32).astype(np.uint8) << 7
-    a = np.abs(x32).astype(np.float64).reshape(-1)
-    grid = E4M3_POSITIVE
-    big = a >= grid[-1]
-    hi = np.searchsorted(grid, a, side="left")          # grid[hi-1] < a <= grid[hi]
-    hi = np.clip(hi, 1, grid.size - 1)
-    lo = hi - 1
-    d_lo = a - grid[lo]                                   # exact in fp64
-    d_hi = grid[hi] - a
-    code = np.where(d_lo < d_hi, lo, hi)
-    tie = d_lo == d_hi
-    code = np.where(tie, np.where((lo & 1) == 0, lo, hi), code)
-    code = np.where(big, grid.size - 1, code)
-    return (code.astype(np.uint8).reshape(x32.shape) | sign)
+    flat = x32.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for s in range(0, flat.size, _CHUNK):
+        part = flat[s:s + _CHUNK]
+        sign = np.signbit(part).astype(np.uint8) << 7
+        out[s:s + _CHUNK] = _nearest_even(E4M3_POSITIVE, np.abs(part).astype(np.float64)) | sign
+    return out.reshape(x32.shape)

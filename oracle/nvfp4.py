@@ -44,6 +44,7 @@ def quantize_blocks(x, g):
     ``x``: fp32 array [..., D] with D a multiple of 16 (R1: blocks run along the
     last axis).  ``g``: the fp32 global scale (> 0, finite).
     Returns (codes uint8 [..., D] with the sign in bit 3, scale bytes uint8 [..., D/16]).
+    Blocks are independent; large inputs are processed a slice of blocks at a time.
     """
     x = np.asarray(x, dtype=np.float32)
     g = np.float32(g)
@@ -52,7 +53,17 @@ def quantize_blocks(x, g):
     d = x.shape[-1]
     if d % BLOCK:
         raise ValueError("last axis must be a multiple of 16")
-    xb = x.reshape(x.shape[:-1] + (d // BLOCK, BLOCK))
+    flat = x.reshape(-1, BLOCK)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scales = np.empty(flat.shape[0], dtype=np.uint8)
+    step = 1 << 16
+    for s in range(0, flat.shape[0], step):
+        codes[s:s + step], scales[s:s + step] = _quantize_block_rows(flat[s:s + step], g)
+    return codes.reshape(x.shape), scales.reshape(x.shape[:-1] + (d // BLOCK,))
+
+
+def _quantize_block_rows(xb, g):
+    """Blocks [n][16] -> (codes [n][16], scale bytes [n]); the steps R5, R6, R8."""
     # R5: block amax -> u = a / fp32(6 g) -> E4M3 (RNE, saturating)
     a = np.max(np.abs(xb), axis=-1)
     six_g = np.float32(np.float32(6.0) * g)
@@ -68,8 +79,7 @@ def quantize_blocks(x, g):
     mag = np.where(zero_scale[..., None], np.uint8(0), mag).astype(np.uint8)
     # R8: sign copied from x
     sign = np.signbit(xb).astype(np.uint8) << 3
-    codes = (mag | sign).reshape(x.shape)
-    return codes, scale_bytes
+    return mag | sign, scale_bytes
 
 
 def dequantize_blocks(codes, scale_bytes, g) -> np.ndarray:
