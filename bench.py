@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark: NVFP4 paged decode attention on one MI355X -- effective KV GB/s (% of HBM peak) + tokens/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long|batch32|ragged|mixed|extend|tiny]
+
+One step is one decode step of the workload's hot path, inputs already resident in HBM:
+  long     split-K NVFP4 decode + log-sum-exp merge, 4 x 131072 tokens, 8 KV / 64 query heads (default)
+  batch32  same path, 32 x 4096 tokens, 8 / 32 heads; three cache copies rotate so that every
+           step reads a cache not touched by the previous two (the 256 MB last-level cache holds one)
+  ragged   64 ragged sequences, fused quantize-append of one token per sequence + decode
+  mixed    28 layers, FP8 at layers 0, 25, 26, 27 and NVFP4 elsewhere, 44 x 8192 tokens
+  extend   per NVFP4 layer of the mixed stack: 16384-token prefix -> FP8 workspace + 2048-token
+           chunk quantize-append (24 layers per step)
+  tiny     1 x 256 tokens (latency-bound)
+
+The timed region is exactly K steps between two device synchronisations; per-step GPU time of the
+decode launches is also taken with HIP events recorded on the launch stream.  Effective KV GB/s =
+NVFP4 (or FP8) bytes the step must read (144 B per token and KV head; 256 B for FP8) / step time.
+The CPU baseline times the fp64 oracle (dequantize + attention, one thread) on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="long", choices=["long", "batch32", "ragged", "mixed", "extend", "tiny"])
+    ap.add_argument("--pages-per-split", type=int, default=0, help="force the split size (0 = planner)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------------------
+def build_layer_cache(nv, wl, layer, dev, fp8=False):
+    """Upload one layer's cached K/V and write it into a new pool with the library's kernels."""
+    import torch
+    from bit_paged_kv_amd import paged
+    k = torch.cat([wl.kv("k", b, layer) for b in range(wl.batch)]).to(dev)
+    v = torch.cat([wl.kv("v", b, layer) for b in range(wl.batch)]).to(dev)
+    slots = torch.from_numpy(np.concatenate([wl.slots(b) for b in range(wl.batch)])).to(dev)
+    if fp8:
+        pool, s1, s2 = paged.build_fp8_cache(k, v, slots, wl.num_pages)
+    else:
+        pool, s1, s2 = paged.build_nvfp4_cache(k, v, slots, wl.num_pages)
+    del k, v
+    return pool, s1, s2
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """Time the oracle's decode (fp64 dequantize + attention, one thread) on whole (sequence, kv head)
+    units of the workload until ~budget_s of CPU work; returns KV GB/s over the sampled bytes."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as o_att
+    from oracle import nvfp4 as o_nv
+    g = wl.group
+    q = wl.q().float().numpy()
+    done_bytes, spent, units = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for b in range(wl.batch):
+            k = wl.kv("k", b).float().numpy()
+            v = wl.kv("v", b).float().numpy()
+            gk = o_nv.global_scale(k)
+            gv = o_nv.global_scale(v)
+            for hk in range(wl.h_kv):
+                ck, sk = o_nv.quantize_blocks(k[:, hk], gk)      # cache contents (not timed)
+                cv, sv = o_nv.quantize_blocks(v[:, hk], gv)
+                t0 = time.perf_counter()
+                kh = o_nv.dequantize_blocks(ck, sk, gk)[:, None]
+                vh = o_nv.dequantize_blocks(cv, sv, gv)[:, None]
+                o_att.decode_attention_one(q[b, hk * g:(hk + 1) * g], kh, vh, wl.sm_scale)
+                spent += time.perf_counter() - t0
+                done_bytes += k.shape[0] * 144
+                units += 1
+                if spent >= budget_s:
+                    break
+            if spent >= budget_s:
+                break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} (sequence, kv head) units of {int(wl.seq_lens[0])} tokens: fp64 dequantize + "
+                      f"softmax attention for {g} query heads each; {done_bytes} KV bytes in {spent:.2f} s; "
+                      f"host {platform.processor() or platform.machine()}"}
+
+
+# ------------------------------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
+                                   "this build (see the sharding notes in DESIGN.md)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import bit_paged_kv_amd as nv
+    import workloads
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.config
+    index = {"tiny": 0, "batch32": 1, "long": 2, "ragged": 3, "mixed": 4, "extend": 4}[name]
+    wl = workloads.config(index)
+    stream = torch.cuda.current_stream(dev)
+    t_setup = time.perf_counter()
+
+    # ---- build the step ------------------------------------------------------------------------
+    if name in ("long", "batch32", "tiny", "ragged"):
+        copies = 3 if name in ("batch32", "tiny") else 1
+        pools = []
+        for c in range(copies):
+            pool, gk, gv = build_layer_cache(nv, wl, 0, dev)
+            pools.append(pool)
+        log(f"cache built in {time.perf_counter() - t_setup:.1f} s ({copies} copies)")
+        pt = torch.from_numpy(wl.page_table).to(dev)
+        sl = torch.from_numpy(wl.total_lens.astype(np.int32)).to(dev)
+        plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), int(wl.total_lens.sum()),
+                              args.pages_per_split)
+        q = wl.q().to(dev)
+        out = torch.empty((wl.batch, wl.h_q, 128), dtype=torch.float32, device=dev)
+        ws = nv.alloc_decode_workspace(wl.batch, wl.h_q, wl.h_kv, plan[1], dev)
+        new_k = wl.new_token("k").to(dev) if wl.append else None
+        new_v = wl.new_token("v").to(dev) if wl.append else None
+        step_bytes = wl.kv_bytes_nvfp4()
+        calls = [nv.prepare_nvfp4_decode(q, pool, gk, gv, pt, sl, wl.sm_scale, plan, wl.h_kv, new_k=new_k,
+                                         new_v=new_v, out=out, workspace=ws)[0] for pool in pools]
+        counter = [0]
+
+        def step():
+            calls[counter[0] % len(calls)].run()
+            counter[0] += 1
+        kernel = "decode_split_kernel<PageNv4> + merge_splits_kernel"
+        desc = (f"{name}: batch {wl.batch}, context {int(wl.seq_lens[0]) if name != 'ragged' else 'ragged'}, "
+                f"{wl.h_kv} KV / {wl.h_q} query heads, head_dim 128, page 16, NVFP4 cache, "
+                f"split-K {plan[1]} x {plan[0]} pages")
+        extra = {"batch": wl.batch, "context_tokens": int(wl.total_lens.sum()), "kv_heads": wl.h_kv,
+                 "q_heads": wl.h_q, "head_dim": 128, "page_size": 16, "cache": "nvfp4",
+                 "pages_per_split": plan[0], "num_splits": plan[1], "cache_copies_rotated": copies,
+                 "fused_append": bool(wl.append)}
+        tokens_per_step = wl.batch
+    elif name == "mixed":
+        pt = torch.from_numpy(wl.page_table).to(dev)
+        sl = torch.from_numpy(wl.total_lens.astype(np.int32)).to(dev)
+        plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), int(wl.total_lens.sum()),
+                              args.pages_per_split)
+        layers = []
+        for layer in range(wl.layers):
+            fp8 = wl.is_fp8(layer)
+            pool, s1, s2 = build_layer_cache(nv, wl, layer, dev, fp8=fp8)
+            layers.append(dict(precision=nv.PREC_FP8 if fp8 else nv.PREC_NVFP4, q=wl.q(layer).to(dev), pool=pool,
+                               k_gscale=s1, v_gscale=s2,
+                               out=torch.empty((wl.batch, wl.h_q, 128), dtype=torch.float32, device=dev)))
+        log(f"28-layer cache built in {time.perf_counter() - t_setup:.1f} s")
+        ws = nv.alloc_decode_workspace(wl.batch, wl.h_q, wl.h_kv, plan[1], dev)
+        n_fp8 = len(wl.fp8_layers)
+        step_bytes = (wl.layers - n_fp8) * wl.kv_bytes_nvfp4() + n_fp8 * wl.kv_bytes_fp8()
+
+        def step():
+            nv.decode_layers(layers, pt, sl, wl.sm_scale, plan, wl.h_kv, workspace=ws)
+        kernel = "28 x (decode_split_kernel + merge_splits_kernel)"
+        desc = (f"mixed: 28 layers (FP8 at {list(wl.fp8_layers)}), batch {wl.batch}, context 8192, "
+                f"8 KV / 32 query heads, split-K {plan[1]} x {plan[0]} pages")
+        extra = {"batch": wl.batch, "context_tokens": int(wl.total_lens.sum()), "layers": wl.layers,
+                 "fp8_layers": list(wl.fp8_layers), "kv_heads": wl.h_kv, "q_heads": wl.h_q,
+                 "pages_per_split": plan[0], "num_splits": plan[1]}
+        tokens_per_step = wl.batch
+    else:  # extend
+        ext = workloads.Workload(name="extend", seed=wl.seed, batch=1, h_kv=wl.h_kv, h_q=wl.h_q,
+                                 seq_lens=[wl.extend_prefix + wl.extend_chunk], chan=wl.chan)
+        nlayers = [l for l in range(wl.layers) if not wl.is_fp8(l)]
+        prefix, chunk = wl.extend_prefix, wl.extend_chunk
+        pt = torch.from_numpy(ext.page_table).to(dev)
+        from bit_paged_kv_amd import paged
+        caches = []
+        slots = torch.from_numpy(ext.slots(0, 0, prefix)).to(dev)
+        for layer in nlayers:
+            k = ext.kv("k", 0, layer, length=prefix).to(dev)
+            v = ext.kv("v", 0, layer, length=prefix).to(dev)
+            pool, gk_l, gv_l = paged.build_nvfp4_cache(k, v, slots, ext.num_pages)
+            ck = wl.chunk("k", layer).to(dev)
+            cv = wl.chunk("v", layer).to(dev)
+            caches.append((pool, gk_l, gv_l, ck, cv))
+            del k, v
+        log(f"extend caches built in {time.perf_counter() - t_setup:.1f} s")
+        chunk_slots = torch.from_numpy(ext.slots(0, prefix, prefix + chunk)).to(dev)
+        prefix_lens = torch.tensor([prefix], dtype=torch.int32, device=dev)
+        offs = torch.tensor([0, prefix], dtype=torch.int32, device=dev)
+        k_ws = torch.empty((prefix + chunk, wl.h_kv, 128), dtype=torch.uint8, device=dev)   # shared by layers
+        v_ws = torch.empty_like(k_ws)
+
+        def step():
+            for pool, gk_l, gv_l, ck, cv in caches:
+                nv.dequant_to_workspace(pool, gk_l, gv_l, pt, prefix_lens, offs, prefix, 6.0 * gk_l, 6.0 * gv_l,
+                                        wl.h_kv, k_ws, v_ws)
+                nv.nvfp4_quantize_append(ck, cv, chunk_slots, gk_l, gv_l, pool)
+        # bytes: read prefix NVFP4 (144 B/token/head), write FP8 workspace (256 B), read chunk bf16 (512 B),
+        # write chunk NVFP4 (144 B)
+        step_bytes = len(caches) * wl.h_kv * (prefix * (144 + 256) + chunk * (512 + 144))
+        kernel = "24 x (nvfp4_to_fp8_ws_kernel + nvfp4_quantize_kernel)"
+        desc = (f"extend: {len(caches)} NVFP4 layers x (16384-token prefix -> shared FP8 workspace + "
+                f"2048-token chunk quantize-append), 8 KV heads")
+        extra = {"layers": len(caches), "prefix": prefix, "chunk": chunk, "kv_heads": wl.h_kv}
+        tokens_per_step = chunk
+
+    # ---- warm up, then time exactly K steps -------------------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps     # HIP events on the launch stream, per step
+    ms_per_step = wall * 1e3 / args.steps
+    achieved = step_bytes / (gpu_ms * 1e-3) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    if name in ("long", "batch32", "tiny", "ragged"):
+        assert torch.isfinite(out).all().item(), "non-finite decode output"
+    log(f"{args.steps} steps: wall {ms_per_step:.4f} ms/step, events {gpu_ms:.4f} ms/step, "
+        f"{achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline and name in ("long", "batch32", "ragged", "tiny"):
+        cpu = cpu_baseline(wl)
+        log(f"cpu baseline {cpu['value']} GB/s")
+
+    traffic = None
+    res = {
+        "metric": "NVFP4 paged decode attn: effective KV GB/s (% of HBM peak) + tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded; see workloads/)",
+        "config": {"workload": desc, **extra},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(tokens_per_step / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                     "timing": "HIP events on the launch stream around the K timed steps, divided by K"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

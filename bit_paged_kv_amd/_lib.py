@@ -45,7 +45,7 @@ EXPORTED = {
     "nvfp4_kv_quantize_append": (_i, [_p, _p, _i, _f, _f, _p, _i, _i, _i, _i, _f, _f, _p, _p, _p, _p, _p]),
     "fp8_kv_quantize_append": (_i, [_p, _p, _p, _i, _i, _i, _i, _f, _f, _p, _p, _p]),
     "nvkv_plan_decode": (_i, [_i, _i, _i, ctypes.c_longlong, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
-    "nvkv_decode_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "nvkv_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "nvfp4_paged_decode_attn": (_i, [_p, _p, _p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i,
                                      _p, _p, _p, _p, _sz, _p]),
     "fp8_paged_decode_attn": (_i, [_p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p, _p, _sz, _p]),
@@ -183,11 +183,17 @@ def plan_decode(batch: int, num_kv_heads: int, max_seq_len: int, total_tokens: i
     return pps.value, ns.value
 
 
-def decode_workspace_size(batch: int, num_q_heads: int, num_splits: int) -> int:
-    return _lib.nvkv_decode_workspace_size(batch, num_q_heads, HEAD_DIM, num_splits)
+def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, num_splits: int) -> int:
+    return _lib.nvkv_decode_workspace_size(batch, num_q_heads, num_kv_heads, HEAD_DIM, num_splits)
 
 
-def _decode_prep(q, page_table, seq_lens, plan, out, workspace):
+def alloc_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, num_splits: int, device):
+    """Workspace for decode partials (uninitialised: the kernels write before they read)."""
+    n = decode_workspace_size(batch, num_q_heads, num_kv_heads, num_splits)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _decode_prep(q, page_table, seq_lens, plan, out, workspace, num_kv_heads):
     _need(q, torch.bfloat16, "q")
     _need(page_table, torch.int32, "page_table")
     _need(seq_lens, torch.int32, "seq_lens")
@@ -200,9 +206,9 @@ def _decode_prep(q, page_table, seq_lens, plan, out, workspace):
     if out is None:
         out = torch.empty((b, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
-    need = decode_workspace_size(b, hq, ns)
+    need = decode_workspace_size(b, hq, num_kv_heads, ns)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = alloc_decode_workspace(b, hq, num_kv_heads, ns, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return b, hq, pps, ns, out, workspace, ws_bytes
 
@@ -211,7 +217,7 @@ def nvfp4_decode(q: torch.Tensor, pool: dict, k_gscale: float, v_gscale: float, 
                  seq_lens: torch.Tensor, sm_scale: float, plan, num_kv_heads: int, new_k=None, new_v=None,
                  out=None, workspace=None) -> torch.Tensor:
     """One decode step over an NVFP4 pool; returns out [batch][H_q][128] fp32."""
-    b, hq, pps, ns, out, workspace, ws_bytes = _decode_prep(q, page_table, seq_lens, plan, out, workspace)
+    b, hq, pps, ns, out, workspace, ws_bytes = _decode_prep(q, page_table, seq_lens, plan, out, workspace, num_kv_heads)
     if new_k is not None:
         _need(new_k, torch.bfloat16, "new_k")
         _need(new_v, torch.bfloat16, "new_v")
@@ -222,9 +228,41 @@ def nvfp4_decode(q: torch.Tensor, pool: dict, k_gscale: float, v_gscale: float, 
     return out
 
 
+class PreparedDecode:
+    """A decode call with every argument marshalled once: ``run()`` is a single C call.
+
+    For serving loops that replay the same step (same buffers, same plan) many times; the tensors
+    passed in are kept alive by this object.
+    """
+
+    def __init__(self, fn, args, keep, stream_of):
+        self._fn = fn
+        self._args = args
+        self._keep = keep
+        self._stream_of = stream_of
+
+    def run(self):
+        st = self._fn(*self._args[:-1], _stream(self._stream_of))
+        if st != 0:
+            _check(self._fn.__name__, st)
+
+
+def prepare_nvfp4_decode(q, pool, k_gscale, v_gscale, page_table, seq_lens, sm_scale, plan, num_kv_heads,
+                         new_k=None, new_v=None, out=None, workspace=None) -> tuple:
+    """Validate once and return (PreparedDecode, out)."""
+    b, hq, pps, ns, out, workspace, ws_bytes = _decode_prep(q, page_table, seq_lens, plan, out, workspace,
+                                                            num_kv_heads)
+    args = (_ptr(q), _ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]), _ptr(pool["v_scale"]),
+            k_gscale, v_gscale, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), b, hq, num_kv_heads,
+            HEAD_DIM, PAGE_SIZE, sm_scale, pps, ns, _ptr(new_k), _ptr(new_v), _ptr(out), _ptr(workspace), ws_bytes,
+            None)
+    keep = (q, pool, page_table, seq_lens, new_k, new_v, out, workspace)
+    return PreparedDecode(_lib.nvfp4_paged_decode_attn, args, keep, q), out
+
+
 def fp8_decode(q: torch.Tensor, pool: dict, k_scale: float, v_scale: float, page_table: torch.Tensor,
                seq_lens: torch.Tensor, sm_scale: float, plan, num_kv_heads: int, out=None, workspace=None):
-    b, hq, pps, ns, out, workspace, ws_bytes = _decode_prep(q, page_table, seq_lens, plan, out, workspace)
+    b, hq, pps, ns, out, workspace, ws_bytes = _decode_prep(q, page_table, seq_lens, plan, out, workspace, num_kv_heads)
     _check("fp8_paged_decode_attn", _lib.fp8_paged_decode_attn(
         _ptr(q), _ptr(pool["k"]), _ptr(pool["v"]), k_scale, v_scale, _ptr(page_table), page_table.shape[1],
         _ptr(seq_lens), b, hq, num_kv_heads, HEAD_DIM, PAGE_SIZE, sm_scale, pps, ns, _ptr(out), _ptr(workspace),
@@ -238,7 +276,8 @@ def decode_layers(layers: list, page_table: torch.Tensor, seq_lens: torch.Tensor
     if not layers:
         raise ValueError("no layers")
     q0 = layers[0]["q"]
-    b, hq, pps, ns, _, workspace, ws_bytes = _decode_prep(q0, page_table, seq_lens, plan, layers[0]["out"], workspace)
+    b, hq, pps, ns, _, workspace, ws_bytes = _decode_prep(q0, page_table, seq_lens, plan, layers[0]["out"], workspace,
+                                                           num_kv_heads)
     arr = (NvkvLayer * len(layers))()
     for i, L in enumerate(layers):
         _need(L["q"], torch.bfloat16, "q")

@@ -70,7 +70,7 @@ int decode_common_status(const void* q, const int32_t* page_table, int max_pages
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4)) return NVKV_E_INVAL;
   if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return NVKV_E_INVAL;
   if (pages_per_split < 1 || num_splits < 1) return NVKV_E_INVAL;
-  const size_t need = nvkv::decode_workspace_bytes(batch, num_q_heads, num_splits);
+  const size_t need = nvkv::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVKV_E_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return NVKV_E_INVAL;
   return NVKV_OK;
@@ -154,25 +154,27 @@ int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long tot
   if (force_pages_per_split > 0) {
     pps = force_pages_per_split;
   } else {
-    // page-heads of the whole step, spread over ~8 wavefronts per compute unit
+    // page-heads of the whole step spread over ~3 four-wave workgroups per compute unit (the
+    // decode kernel's occupancy)
     const long long seq_pages = total_tokens > 0 ? (total_tokens + (long long)batch * (kPage - 1)) / kPage
                                                  : (long long)batch * max_pages;
     const long long work = seq_pages * num_kv_heads;
-    const long long target = (long long)device_cus() * 8;
+    const long long target = (long long)device_cus() * 3;
     pps = std::max<long long>(8, (work + target - 1) / target);
+    pps = (pps + 7) & ~7LL;                             // whole pairs of pages for each of the 4 waves
   }
-  pps = (pps + 1) & ~1LL;                               // whole pairs of pages
+  pps = (pps + 1) & ~1LL;
   pps = std::min<long long>(pps, std::max<long long>(2, (max_pages + 1) & ~1LL));
   const long long splits = (max_pages + pps - 1) / pps;
-  if (splits > 65535LL * 4) return NVKV_E_UNSUPPORTED;
+  if (splits > 0x7FFFFFFFLL) return NVKV_E_UNSUPPORTED;
   *pages_per_split = (int)pps;
   *num_splits = (int)std::max<long long>(1, splits);
   return NVKV_OK;
 }
 
-size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int head_dim, int num_splits) {
-  if (batch < 1 || num_q_heads < 1 || head_dim != kD || num_splits < 1) return 0;
-  return nvkv::decode_workspace_bytes(batch, num_q_heads, num_splits);
+size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim, int num_splits) {
+  if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim != kD || num_splits < 1) return 0;
+  return nvkv::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, num_splits);
 }
 
 int nvfp4_paged_decode_attn(const void* q, const uint8_t* k_data, const uint8_t* k_scale, const uint8_t* v_data,

@@ -40,7 +40,7 @@ struct PageNv4 {
   uint4 kd;      // 32 E2M1 codes of token (lane % 16), channels 32*(lane/16) .. +31
   uint32_t ks;   // their two E4M3 block scales (low 16 bits)
   uint4 vd;      // 32 E2M1 codes: tokens 4*(lane/16) .. +3 at channels 16n + lane%16, n = 0..7
-  uint4 vs0, vs1;  // E4M3 scales of tokens 4*(lane/16) .. +3, blocks 0..7 (dword n = block n)
+  uint32_t vs;   // V scale bytes 2*lane, 2*lane+1: tokens 4*(lane/16) + 2*(lane%2) + {0,1}, block (lane%16)/2
 };
 struct PageFp8 {
   uint4 k0, k1;  // 32 E4M3 values of token (lane % 16), channels 32*(lane/16) .. +31
@@ -51,24 +51,23 @@ __device__ __forceinline__ void zero_page(PageNv4& p) {
   p.kd = make_uint4(0, 0, 0, 0);
   p.ks = 0;
   p.vd = make_uint4(0, 0, 0, 0);
-  p.vs0 = make_uint4(0, 0, 0, 0);
-  p.vs1 = make_uint4(0, 0, 0, 0);
+  p.vs = 0;
 }
 __device__ __forceinline__ void zero_page(PageFp8& p) {
   p.k0 = p.k1 = p.v0 = p.v1 = make_uint4(0, 0, 0, 0);
 }
 
-__device__ __forceinline__ void load_page(PageNv4& p, const DecodeArgs& a, size_t blk, int lane) {
-  p.kd = *reinterpret_cast<const uint4*>(a.k_data + blk * kNvfp4DataBytes + lane * 16);
-  p.ks = *reinterpret_cast<const uint16_t*>(a.k_scale + blk * kNvfp4ScaleBytes + lane * 2);
-  p.vd = *reinterpret_cast<const uint4*>(a.v_data + blk * kNvfp4DataBytes + lane * 16);
-  const uint4* vs = reinterpret_cast<const uint4*>(a.v_scale + blk * kNvfp4ScaleBytes + (lane >> 4) * 32);
-  p.vs0 = vs[0];
-  p.vs1 = vs[1];
+// blk is wave-uniform and the lane offset an unsigned 32-bit value, so each load is a single
+// global_load with a scalar base and a vector offset (no per-load 64-bit address arithmetic).
+__device__ __forceinline__ void load_page(PageNv4& p, const DecodeArgs& a, size_t blk, unsigned lane) {
+  p.kd = *reinterpret_cast<const uint4*>(a.k_data + blk * kNvfp4DataBytes + lane * 16u);
+  p.ks = *reinterpret_cast<const uint16_t*>(a.k_scale + blk * kNvfp4ScaleBytes + lane * 2u);
+  p.vd = *reinterpret_cast<const uint4*>(a.v_data + blk * kNvfp4DataBytes + lane * 16u);
+  p.vs = *reinterpret_cast<const uint16_t*>(a.v_scale + blk * kNvfp4ScaleBytes + lane * 2u);
 }
-__device__ __forceinline__ void load_page(PageFp8& p, const DecodeArgs& a, size_t blk, int lane) {
-  const uint4* k = reinterpret_cast<const uint4*>(a.k_data + blk * kFp8Bytes + lane * 32);
-  const uint4* v = reinterpret_cast<const uint4*>(a.v_data + blk * kFp8Bytes + lane * 32);
+__device__ __forceinline__ void load_page(PageFp8& p, const DecodeArgs& a, size_t blk, unsigned lane) {
+  const uint4* k = reinterpret_cast<const uint4*>(a.k_data + blk * kFp8Bytes + lane * 32u);
+  const uint4* v = reinterpret_cast<const uint4*>(a.v_data + blk * kFp8Bytes + lane * 32u);
   p.k0 = k[0];
   p.k1 = k[1];
   p.v0 = v[0];
@@ -81,12 +80,8 @@ __device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v
 // written (possibly NaN scale patterns) cannot reach the arithmetic.
 __device__ __forceinline__ void mask_page(PageNv4& p, int nvalid, int lane) {
   if ((lane & 15) >= nvalid) p.ks = 0;                     // K: scale 0 -> exact zeros
-  const int t0 = 4 * (lane >> 4);
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m |= (t0 + i < nvalid ? 0xFFu : 0u) << (8 * i);
-  p.vs0 = and4(p.vs0, m);                                  // V: per-token scale bytes
-  p.vs1 = and4(p.vs1, m);
+  const int t0 = 4 * (lane >> 4) + 2 * (lane & 1);         // V: the two tokens of this lane's scale bytes
+  p.vs &= (t0 < nvalid ? 0xFFu : 0u) | (t0 + 1 < nvalid ? 0xFF00u : 0u);
 }
 __device__ __forceinline__ void mask_page(PageFp8& p, int nvalid, int lane) {
   if ((lane & 15) >= nvalid) p.k0 = p.k1 = make_uint4(0, 0, 0, 0);
@@ -116,33 +111,42 @@ __device__ __forceinline__ h2 k_scales(const PageNv4& p) { return fp8x2_to_h2<fa
 __device__ __forceinline__ h2 k_scales(const PageFp8&) { return h2{(_Float16)1.0f, (_Float16)1.0f}; }
 
 // --- V operands: A[channel 16N + lane%16][k], k = tokens 4*(lane/16)+0..3 of page 0, then page 1 ---
+// sc0 / sc1: the 16 fp16 scale pairs of this lane's token quad (dword 2n + h = tokens +2h, +2h+1 of
+// block n) for page 0 / page 1, gathered through LDS (v_scale_pairs below).
 template <int N>
-__device__ __forceinline__ h8 v_operand(const PageNv4& p0, const PageNv4& p1) {
+__device__ __forceinline__ h8 v_operand(const PageNv4& p0, const PageNv4& p1, const uint4 (&sc0)[4],
+                                        const uint4 (&sc1)[4]) {
   constexpr int W = N >> 1;           // dword holding block N
   constexpr int B0 = 2 * (N & 1);     // byte of tokens (+0,+1); B0 + 1 holds tokens (+2,+3)
   const uint32_t d0 = u4get(p0.vd, W), d1 = u4get(p1.vd, W);
-  const uint32_t s0 = (N < 4) ? u4get(p0.vs0, N & 3) : u4get(p0.vs1, N & 3);
-  const uint32_t s1 = (N < 4) ? u4get(p1.vs0, N & 3) : u4get(p1.vs1, N & 3);
-  return cat4(fp4x2_to_h2<B0>(d0) * fp8x2_to_h2<false>(s0), fp4x2_to_h2<B0 + 1>(d0) * fp8x2_to_h2<true>(s0),
-              fp4x2_to_h2<B0>(d1) * fp8x2_to_h2<false>(s1), fp4x2_to_h2<B0 + 1>(d1) * fp8x2_to_h2<true>(s1));
+  const h2 s00 = __builtin_bit_cast(h2, u4get(sc0[N >> 1], 2 * (N & 1)));
+  const h2 s01 = __builtin_bit_cast(h2, u4get(sc0[N >> 1], 2 * (N & 1) + 1));
+  const h2 s10 = __builtin_bit_cast(h2, u4get(sc1[N >> 1], 2 * (N & 1)));
+  const h2 s11 = __builtin_bit_cast(h2, u4get(sc1[N >> 1], 2 * (N & 1) + 1));
+  return cat4(fp4x2_to_h2<B0>(d0) * s00, fp4x2_to_h2<B0 + 1>(d0) * s01,
+              fp4x2_to_h2<B0>(d1) * s10, fp4x2_to_h2<B0 + 1>(d1) * s11);
 }
 template <int N>
-__device__ __forceinline__ h8 v_operand(const PageFp8& p0, const PageFp8& p1) {
+__device__ __forceinline__ h8 v_operand(const PageFp8& p0, const PageFp8& p1, const uint4 (&)[4],
+                                        const uint4 (&)[4]) {
   const uint32_t a = (N < 4) ? u4get(p0.v0, N & 3) : u4get(p0.v1, N & 3);
   const uint32_t b = (N < 4) ? u4get(p1.v0, N & 3) : u4get(p1.v1, N & 3);
   return cat4(fp8x2_to_h2<false>(a), fp8x2_to_h2<true>(a), fp8x2_to_h2<false>(b), fp8x2_to_h2<true>(b));
 }
 
-template <typename Page>
-__device__ __forceinline__ f4 qk_page(const Page& p, const h8 (&qb)[4]) {
-  const h2 sc2 = k_scales(p);
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<0>(p, sc2), qb[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<1>(p, sc2), qb[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<2>(p, sc2), qb[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p, sc2), qb[3], acc, 0, 0, 0);
-  return acc;
+// Each lane converts the E4M3 pair it loaded (tokens 4c + 2(lane%2) + {0,1} of block (lane%16)/2)
+// and the 16 lanes of a token quad c exchange their pairs through this wave's LDS slot: lane c*16+x
+// reads back the 16 pairs of quad c in (block, half) order.  LDS operations of one wave complete in
+// order, so no barrier is needed.
+__device__ __forceinline__ void v_scale_pairs(const PageNv4& p, uint32_t* slot, int lane, uint4 (&out)[4]) {
+  slot[lane] = __builtin_bit_cast(uint32_t, fp8x2_to_h2<false>(p.vs));
+  const uint4* src = reinterpret_cast<const uint4*>(slot + 16 * (lane >> 4));
+  out[0] = src[0];
+  out[1] = src[1];
+  out[2] = src[2];
+  out[3] = src[3];
 }
+__device__ __forceinline__ void v_scale_pairs(const PageFp8&, uint32_t*, int, uint4 (&)[4]) {}
 
 // Fused quantize-append of one new token (position pos) of kv head hk into the NVFP4 pools.
 // Lanes 0..31 handle K, 32..63 V; four lanes share a 16-channel block (4 channels each).
@@ -184,19 +188,30 @@ __device__ void append_token_nvfp4(const DecodeArgs& a, int b, int hk, int pos, 
   }
 }
 
+// Workspace of a multi-split decode: per (row = b * Hq + h, split) the unnormalised partial output
+// [128] (times g_V), then per (row, split) its (max, sum) in log2 units.
 template <typename Page>
-__global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int split = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (split >= a.num_splits) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x;
   const int hk = blockIdx.y, b = blockIdx.z;
   const int group = a.hq / a.hkv;
   const int seq_len = a.seq_lens[b];
   const int n_pages = (seq_len + kPageSize - 1) / kPageSize;
-  const int pg_begin = split * a.pages_per_split;
-  const int pg_end = (split == a.num_splits - 1) ? n_pages : min(n_pages, pg_begin + a.pages_per_split);
+  // this workgroup's pages; the last split also takes any remainder
+  const int wg_begin = min(split * a.pages_per_split, n_pages);
+  const int wg_end = (split == a.num_splits - 1) ? n_pages : min(n_pages, wg_begin + a.pages_per_split);
+  // each wave takes a contiguous, even-sized quarter of them
+  const int quarter = (((wg_end - wg_begin + kWaves - 1) / kWaves) + 1) & ~1;
+  const int pg_begin = min(wg_end, wg_begin + wave * quarter);
+  const int pg_end = min(wg_end, pg_begin + quarter);
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
   const int jh = lane & 15, c = lane >> 4;
+  __shared__ uint32_t vs_lds[kWaves][128];                  // per-wave exchange slot for V scale pairs
+  __shared__ float red_o[kWaves][16][kHeadDim];             // per-wave partial outputs
+  __shared__ float red_ml[kWaves][16][2];                   // per-wave (max, sum) per query head
+  uint32_t* vs_slot = vs_lds[wave];
   const bool head_ok = jh < group;
   const int hq = hk * group + (head_ok ? jh : 0);
   const size_t row = (size_t)b * a.hq + hq;
@@ -204,173 +219,294 @@ __global__ __launch_bounds__(64 * kWaves) void decode_split_kernel(DecodeArgs a)
   if constexpr (std::is_same<Page, PageNv4>::value) {
     if (a.new_k != nullptr) {
       const int pos = seq_len - 1;
-      const int owner = min((pos / kPageSize) / a.pages_per_split, a.num_splits - 1);
-      if (split == owner) {
+      if (pos / kPageSize >= pg_begin && pos / kPageSize < pg_end) {
         append_token_nvfp4(a, b, hk, pos, pt[pos / kPageSize], lane);
-        __threadfence();   // the stores must be visible to this wave's loads of the page below
+        // only this wave reads the page back; its stores reach L2 (L1 writes through, and L1 holds no
+        // copy of the page: it is invalidated at kernel start), so waiting for them suffices
+        __threadfence_block();
       }
     }
   }
-
-  float* part_o = reinterpret_cast<float*>(a.workspace);
-  float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
-  if (pg_begin >= pg_end) {   // a split past the end of a short sequence (num_splits > 1 only)
-    if (head_ok && c == 0) {
-      float2 ml = make_float2(-INFINITY, 0.0f);
-      *reinterpret_cast<float2*>(part_ml + (row * a.num_splits + split) * 2) = ml;
-    }
-    return;
-  }
-
-  // q row -> fp16 B operands, rescaled by a power of two so the row maximum sits in [2^13, 2^14)
-  float qf[32];
-  if (head_ok) {
-    const uint4* qp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + row * kHeadDim + 32 * c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bf16x8_to_f32(qp[i], qf + 8 * i);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
-  }
-  float qmax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qf[i]));
-  qmax = wave_max_xor(qmax, 16);
-  qmax = wave_max_xor(qmax, 32);
-  int qexp = 0;
-  if (qmax > 0.0f) {
-    int ex;
-    (void)frexpf(qmax, &ex);          // qmax = f * 2^ex, f in [0.5, 1)
-    qexp = min(max(14 - ex, -100), 100);
-  }
-  h8 qb[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qb[s][i] = (_Float16)__builtin_ldexpf(qf[8 * s + i], qexp);
-  // scores in log2 units: <q, K_hat> * sm_scale * log2(e); K_hat = (e2m1 * s_blk) * g_K
-  const float qk_scale = a.sm_scale * 1.44269504088896341f * a.k_gscale * __builtin_ldexpf(1.0f, -qexp);
 
   float m_run = -INFINITY, l_run = 0.0f;
   f4 o[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) o[n] = f4{0.f, 0.f, 0.f, 0.f};
 
-  Page cur0, cur1, nxt0, nxt1;
-  auto load_pair = [&](Page& p0, Page& p1, int pg, int id0, int id1) {
-    load_page(p0, a, (size_t)id0 * a.hkv + hk, lane);
-    if (pg + 1 < pg_end) load_page(p1, a, (size_t)id1 * a.hkv + hk, lane);
-    else zero_page(p1);
-  };
-  int id_n0 = pt[pg_begin], id_n1 = pt[min(pg_begin + 1, pg_end - 1)];
-  load_pair(cur0, cur1, pg_begin, id_n0, id_n1);
-  id_n0 = pt[min(pg_begin + 2, pg_end - 1)];
-  id_n1 = pt[min(pg_begin + 3, pg_end - 1)];
-
-  for (int pg = pg_begin; pg < pg_end; pg += 2) {
-    // issue the next pair's loads (and the page ids after it) before computing this pair
-    const int id_f0 = pt[min(pg + 4, pg_end - 1)];
-    const int id_f1 = pt[min(pg + 5, pg_end - 1)];
-    if (pg + 2 < pg_end) load_pair(nxt0, nxt1, pg + 2, id_n0, id_n1);
-
-    const int nv0 = min(kPageSize, seq_len - pg * kPageSize);
-    const int nv1 = (pg + 1 < pg_end) ? min(kPageSize, seq_len - (pg + 1) * kPageSize) : 0;
-    if (nv0 < kPageSize) mask_page(cur0, nv0, lane);
-    if (nv1 < kPageSize && nv1 > 0) mask_page(cur1, nv1, lane);
-
-    const f4 s0 = qk_page(cur0, qb);
-    const f4 s1 = (nv1 > 0) ? qk_page(cur1, qb) : f4{0.f, 0.f, 0.f, 0.f};
-    float x[8];
+  if (pg_begin < pg_end) {
+    // q row -> fp16 B operands, rescaled by a power of two so the row maximum sits in [2^13, 2^14)
+    float qf[32];
+    if (head_ok) {
+      const uint4* qp =
+          reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + row * kHeadDim + 32 * c);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = (4 * c + r < nv0) ? s0[r] * qk_scale : -INFINITY;
-      x[4 + r] = (4 * c + r < nv1) ? s1[r] * qk_scale : -INFINITY;
+      for (int i = 0; i < 4; ++i) bf16x8_to_f32(qp[i], qf + 8 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
     }
-    float mloc = x[0];
+    float qmax = 0.0f;
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mloc = fmaxf(mloc, x[i]);
-    mloc = wave_max_xor(mloc, 16);
-    mloc = wave_max_xor(mloc, 32);
-    const float m_new = fmaxf(m_run, mloc);
-    if (__any(m_new > m_run)) {     // rescale only when some head's running max moved
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) o[n] *= alpha;
+    for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qf[i]));
+    qmax = wave_max_xor(qmax, 16);
+    qmax = wave_max_xor(qmax, 32);
+    int qexp = 0;
+    if (qmax > 0.0f) {
+      int ex;
+      (void)frexpf(qmax, &ex);          // qmax = f * 2^ex, f in [0.5, 1)
+      qexp = min(max(14 - ex, -100), 100);
     }
-    m_run = m_new;
-    float pr[8];
-    float psum = 0.0f;
+    h8 qb[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pr[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
-      psum += pr[i];
-    }
-    l_run += psum;
-    h8 ph, pl;
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ph[i] = (_Float16)pr[i];
-      pl[i] = (_Float16)(pr[i] - (float)ph[i]);
-    }
-    static_for<0, 8>([&](auto nc) {
-      constexpr int N = decltype(nc)::value;
-      const h8 va = v_operand<N>(cur0, cur1);
-      o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, o[N], 0, 0, 0);
-      o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pl, o[N], 0, 0, 0);
-    });
+      for (int i = 0; i < 8; ++i) qb[s][i] = (_Float16)__builtin_ldexpf(qf[8 * s + i], qexp);
+    // scores in log2 units: <q, K_hat> * sm_scale * log2(e); K_hat = (e2m1 * s_blk) * g_K
+    const float qk_scale = a.sm_scale * 1.44269504088896341f * a.k_gscale * __builtin_ldexpf(1.0f, -qexp);
 
-    cur0 = nxt0;
-    cur1 = nxt1;
-    id_n0 = id_f0;
-    id_n1 = id_f1;
+    // Every load below is unconditional: a pair index past the end is clamped to the last pair (a
+    // re-read that hits in cache) and an odd trailing page is masked, so no branch separates a load
+    // from its use and the waits on the vector-memory counter stay precise while two pairs are in flight.
+    const int npairs = (pg_end - pg_begin + 1) >> 1;
+    int vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));   // per-lane zero: keeps page-id loads on the vector path
+    const int32_t* ptw = pt + pg_begin + vzero;
+    auto load_ids = [&](int pair, int& i0, int& i1) {
+      const int rel = 2 * min(pair, npairs - 1);
+      i0 = ptw[rel];
+      i1 = ptw[min(rel + 1, pg_end - pg_begin - 1)];
+    };
+    auto issue = [&](Page& p0, Page& p1, int i0, int i1) {
+      load_page(p0, a, (size_t)__builtin_amdgcn_readfirstlane(i0) * a.hkv + hk, (unsigned)lane);
+      load_page(p1, a, (size_t)__builtin_amdgcn_readfirstlane(i1) * a.hkv + hk, (unsigned)lane);
+    };
+
+    // One pair of pages: S^T = K_hat q^T, online softmax, O^T += V_hat^T P^T.  Only the last pair of
+    // a wave's range can hold a partly filled or missing page (tail): masking runs only there.
+    auto process = [&](Page& p0, Page& p1, int pair, bool tail) {
+      const int pg = pg_begin + 2 * pair;
+      int nv0 = kPageSize, nv1 = kPageSize;
+      if (tail) {
+        asm volatile("" ::: "memory");   // keep this a branch: the masking must not run on every pair
+        nv0 = min(kPageSize, seq_len - pg * kPageSize);
+        nv1 = (pg + 1 < pg_end) ? min(kPageSize, seq_len - (pg + 1) * kPageSize) : 0;
+        if (nv0 < kPageSize) mask_page(p0, nv0, lane);
+        if (nv1 < kPageSize) mask_page(p1, nv1, lane);   // nv1 == 0: a duplicated page, all masked
+      }
+      // two independent MFMA chains (one per page), interleaved
+      const h2 sc0 = k_scales(p0), sc1 = k_scales(p1);
+      f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<0>(p0, sc0), qb[0], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<0>(p1, sc1), qb[0], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<1>(p0, sc0), qb[1], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<1>(p1, sc1), qb[1], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<2>(p0, sc0), qb[2], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<2>(p1, sc1), qb[2], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p0, sc0), qb[3], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p1, sc1), qb[3], s1, 0, 0, 0);
+      // raw scores; qk_scale > 0, so the maximum can be taken before scaling
+      float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      if (tail) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (4 * c + r >= nv0) x[r] = -INFINITY;
+          if (4 * c + r >= nv1) x[4 + r] = -INFINITY;
+        }
+      }
+      float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mloc = wave_max_xor(mloc, 16);
+      mloc = wave_max_xor(mloc, 32);
+      const float m_new = fmaxf(m_run, mloc * qk_scale);
+      if (__any(m_new > m_run)) {     // rescale only when some head's running max moved
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) o[n] *= alpha;
+      }
+      m_run = m_new;
+      float pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk_scale, -m_new));
+      l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+      h8 ph, pl;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ph[i] = (_Float16)pr[i];
+        pl[i] = (_Float16)(pr[i] - (float)ph[i]);
+      }
+      // PV: hi product of block N issued next to the lo product of block N-1
+      uint4 vsc0[4], vsc1[4];
+      v_scale_pairs(p0, vs_slot, lane, vsc0);
+      v_scale_pairs(p1, vs_slot + 64, lane, vsc1);
+      h8 va_prev;
+      static_for<0, 8>([&](auto nc) {
+        constexpr int N = decltype(nc)::value;
+        const h8 va = v_operand<N>(p0, p1, vsc0, vsc1);
+        o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, o[N], 0, 0, 0);
+        if constexpr (N > 0) o[N - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[N - 1], 0, 0, 0);
+        va_prev = va;
+      });
+      o[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[7], 0, 0, 0);
+    };
+
+    if constexpr (std::is_same<Page, PageNv4>::value) {
+      // Three register buffers in rotation: two pairs are in flight while one is computed; page ids
+      // are fetched one pair ahead of the data that needs them.
+      Page pa0, pa1, pb0, pb1, pc0, pc1;
+      int a0, a1, b0, b1, c0, c1;
+      load_ids(0, a0, a1);
+      load_ids(1, b0, b1);
+      load_ids(2, c0, c1);
+      issue(pa0, pa1, a0, a1);
+      issue(pb0, pb1, b0, b1);
+      for (int pr = 0;; pr += 3) {
+        load_ids(pr + 3, a0, a1);
+        issue(pc0, pc1, c0, c1);
+        process(pa0, pa1, pr, pr + 1 >= npairs);
+        if (pr + 1 >= npairs) break;
+        load_ids(pr + 4, b0, b1);
+        issue(pa0, pa1, a0, a1);
+        process(pb0, pb1, pr + 1, pr + 2 >= npairs);
+        if (pr + 2 >= npairs) break;
+        load_ids(pr + 5, c0, c1);
+        issue(pb0, pb1, b0, b1);
+        process(pc0, pc1, pr + 2, pr + 3 >= npairs);
+        if (pr + 3 >= npairs) break;
+      }
+    } else {
+      // FP8 pages take twice the registers: two buffers, one pair in flight while one is computed.
+      Page pa0, pa1, pb0, pb1;
+      int a0, a1, b0, b1;
+      load_ids(0, a0, a1);
+      load_ids(1, b0, b1);
+      issue(pa0, pa1, a0, a1);
+      for (int pr = 0;; pr += 2) {
+        load_ids(pr + 2, a0, a1);
+        issue(pb0, pb1, b0, b1);
+        process(pa0, pa1, pr, pr + 1 >= npairs);
+        if (pr + 1 >= npairs) break;
+        load_ids(pr + 3, b0, b1);
+        issue(pa0, pa1, a0, a1);
+        process(pb0, pb1, pr + 1, pr + 2 >= npairs);
+        if (pr + 2 >= npairs) break;
+      }
+    }
+    l_run = wave_sum_xor(l_run, 16);
+    l_run = wave_sum_xor(l_run, 32);
   }
 
-  l_run = wave_sum_xor(l_run, 16);
-  l_run = wave_sum_xor(l_run, 32);
-  if (!head_ok) return;
-  // lane holds O^T[16n + 4c + r][head]
+  // ---- combine the 4 waves of this workgroup (lane holds O^T[16n + 4c + r][head jh]) ----
+#pragma unroll
+  for (int n = 0; n < 8; ++n) *reinterpret_cast<f4*>(&red_o[wave][jh][16 * n + 4 * c]) = o[n];
+  if (c == 0) {
+    red_ml[wave][jh][0] = m_run;
+    red_ml[wave][jh][1] = l_run;
+  }
+  __syncthreads();
+  const int tj = threadIdx.x >> 4;            // query head (within the group) of this thread
+  const int td = (threadIdx.x & 15) * 8;      // first of its 8 channels
+  const bool t_ok = tj < group;
+  const size_t trow = (size_t)b * a.hq + hk * group + (t_ok ? tj : 0);
+  float cm = -INFINITY, cl = 0.0f, co[8];
+  if (t_ok) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (red_ml[w][tj][1] > 0.0f) cm = fmaxf(cm, red_ml[w][tj][0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) co[i] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float lw = red_ml[w][tj][1];
+      if (lw > 0.0f) {
+        const float wt = __builtin_amdgcn_exp2f(red_ml[w][tj][0] - cm);
+        cl += wt * lw;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) co[i] += wt * red_o[w][tj][td + i];
+      }
+    }
+  }
   if (a.num_splits == 1) {
-    const float f = a.v_gscale / l_run;
-    float* dst = a.out + row * kHeadDim + 4 * c;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) *reinterpret_cast<f4*>(dst + 16 * n) = o[n] * f;
-  } else {
-    float* dst = part_o + (row * a.num_splits + split) * kHeadDim + 4 * c;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) *reinterpret_cast<f4*>(dst + 16 * n) = o[n] * a.v_gscale;
-    if (c == 0) *reinterpret_cast<float2*>(part_ml + (row * a.num_splits + split) * 2) = make_float2(m_run, l_run);
+    if (t_ok) {
+      const float f = a.v_gscale / cl;
+      float* dst = a.out + trow * kHeadDim + td;
+      *reinterpret_cast<f4*>(dst) = f4{co[0], co[1], co[2], co[3]} * f;
+      *reinterpret_cast<f4*>(dst + 4) = f4{co[4], co[5], co[6], co[7]} * f;
+    }
+    return;
+  }
+
+  // ---- several splits: publish this workgroup's partial for the merge kernel ----
+  float* part_o = reinterpret_cast<float*>(a.workspace);
+  float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
+  if (t_ok) {
+    float* dst = part_o + (trow * a.num_splits + split) * kHeadDim + td;
+    *reinterpret_cast<f4*>(dst) = f4{co[0], co[1], co[2], co[3]} * a.v_gscale;
+    *reinterpret_cast<f4*>(dst + 4) = f4{co[4], co[5], co[6], co[7]} * a.v_gscale;
+    if (td == 0) *reinterpret_cast<float2*>(part_ml + (trow * a.num_splits + split) * 2) = make_float2(cm, cl);
   }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, query head): 128 threads, one channel each.
-__global__ __launch_bounds__(128) void merge_splits_kernel(const float* __restrict__ part_o,
+// Log-sum-exp merge of the splits of one (sequence, query head) per block: 8 groups of 32 threads
+// each walk every 8th split with a running maximum (4 channels per thread), then the 8 group
+// states are combined through LDS.  Spreading the splits over lanes keeps the load chains short.
+constexpr int kMergeGroups = 8;
+__global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int num_splits,
                                                            float* __restrict__ out) {
   const size_t row = blockIdx.x;
-  const float* ml = part_ml + row * num_splits * 2;
-  float m = -INFINITY;
-  for (int s = 0; s < num_splits; ++s)
-    if (ml[2 * s + 1] > 0.0f) m = fmaxf(m, ml[2 * s]);
-  float den = 0.0f, acc = 0.0f;
-  for (int s = 0; s < num_splits; ++s) {
-    const float l = ml[2 * s + 1];
-    if (l > 0.0f) {   // empty splits carry no partial output
-      const float w = __builtin_amdgcn_exp2f(ml[2 * s] - m);
-      den += w * l;
-      acc += w * part_o[(row * num_splits + s) * kHeadDim + threadIdx.x];
+  const int g = threadIdx.x >> 5;
+  const int d = (threadIdx.x & 31) * 4;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + row * num_splits;
+  const float* po = part_o + row * num_splits * kHeadDim + d;
+  float m = -INFINITY, den = 0.0f;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = g; s < num_splits; s += kMergeGroups) {
+    const float2 v = ml[s];
+    const f4 ov = *reinterpret_cast<const f4*>(po + (size_t)s * kHeadDim);
+    if (v.y > 0.0f) {   // empty splits carry no partial output
+      const float m_new = fmaxf(m, v.x);
+      const float f_old = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
+      const float f_new = __builtin_amdgcn_exp2f(v.x - m_new);
+      den = den * f_old + v.y * f_new;
+      acc = acc * f_old + ov * f_new;
+      m = m_new;
     }
   }
-  out[row * kHeadDim + threadIdx.x] = acc / den;
+  __shared__ float g_m[kMergeGroups], g_den[kMergeGroups];
+  __shared__ f4 g_acc[kMergeGroups][32];
+  if ((threadIdx.x & 31) == 0) {
+    g_m[g] = m;
+    g_den[g] = den;
+  }
+  g_acc[g][threadIdx.x & 31] = acc;
+  __syncthreads();
+  if (g != 0) return;
+  float mm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMergeGroups; ++i)
+    if (g_den[i] > 0.0f) mm = fmaxf(mm, g_m[i]);
+  float dd = 0.0f;
+  f4 aa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kMergeGroups; ++i) {
+    if (g_den[i] > 0.0f) {
+      const float w = __builtin_amdgcn_exp2f(g_m[i] - mm);
+      dd += w * g_den[i];
+      aa += w * g_acc[i][threadIdx.x];
+    }
+  }
+  *reinterpret_cast<f4*>(out + row * kHeadDim + d) = aa * (1.0f / dd);
 }
 
-size_t decode_workspace_bytes(int batch, int hq, int num_splits) {
+size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits) {
+  (void)hkv;
   if (num_splits <= 1) return 0;
   return (size_t)batch * hq * num_splits * (kHeadDim + 2) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid((a.num_splits + kWaves - 1) / kWaves, a.hkv, a.batch);
+  dim3 grid(a.num_splits, a.hkv, a.batch);
   if (a.format == kFmtNvfp4)
     hipLaunchKernelGGL(decode_split_kernel<PageNv4>, grid, dim3(64 * kWaves), 0, stream, a);
   else
@@ -379,8 +515,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (e != hipSuccess || a.num_splits == 1) return e;
   const float* part_o = reinterpret_cast<const float*>(a.workspace);
   const float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
-  hipLaunchKernelGGL(merge_splits_kernel, dim3(a.batch * a.hq), dim3(kHeadDim), 0, stream, part_o, part_ml,
-                     a.num_splits, a.out);
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(a.batch * a.hq), dim3(256), 0, stream, part_o, part_ml, a.num_splits,
+                     a.out);
   return hipGetLastError();
 }
 

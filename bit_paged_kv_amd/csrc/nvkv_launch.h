@@ -23,8 +23,8 @@ hipError_t launch_dequant_to_ws(const uint8_t* k_data, const uint8_t* k_scale, c
                                 int max_prefix, float sk_ws, float sv_ws, uint8_t* k_ws, uint8_t* v_ws,
                                 hipStream_t stream);
 
-// Decode: one wavefront per (sequence, kv head, split); partial softmax states are merged by a
-// second kernel when num_splits > 1.
+// Decode: one workgroup of four wavefronts per (sequence, kv head, split); with several splits a
+// second kernel merges the partial softmax states.
 enum CacheFormat { kFmtNvfp4 = 0, kFmtFp8 = 1 };
 
 struct DecodeArgs {
@@ -47,7 +47,7 @@ struct DecodeArgs {
   void* workspace;            // partials when num_splits > 1
 };
 
-size_t decode_workspace_bytes(int batch, int hq, int num_splits);
+size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace nvkv

@@ -120,8 +120,10 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
 
 /*
  * Split planning for decode.  The sequence axis is cut into splits of `pages_per_split` pages;
- * each (sequence, kv head, split) is one wavefront; partial softmax states are merged by a second
- * kernel.  nvkv_plan_decode picks the split from host-side hints so that the grid fills the GPU:
+ * each (sequence, kv head, split) is one workgroup of four wavefronts (each takes a contiguous
+ * quarter of the split and the four combine in LDS); with several splits a second kernel merges the
+ * partial softmax states.  nvkv_plan_decode picks the split from host-side hints so that the grid
+ * fills the GPU:
  *   max_seq_len  : the longest sequence (tokens, including an appended token), > 0.
  *   total_tokens : sum of sequence lengths if known, else 0 (then batch * max_seq_len is assumed).
  *   force_pages_per_split : > 0 forces the split size (rounded up to even); 0 = automatic.
@@ -132,8 +134,9 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
 NVKV_API int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long total_tokens,
                      int force_pages_per_split, int* pages_per_split, int* num_splits);
 
-/* Workspace bytes for decode with the given plan (0 when num_splits == 1). */
-NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int head_dim, int num_splits);
+/* Workspace bytes for decode with the given plan (0 when num_splits == 1); contents need no init. */
+NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                           int num_splits);
 
 /*
  * nvfp4_paged_decode_attn -- one decode step of attention reading the NVFP4 cache directly.

@@ -1,0 +1,172 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function that
+include/nvkv.h declares, plans splits consistently, and rejects bad arguments before any launch.
+
+Every call below is invalid on purpose and must fail validation; no kernel is ever launched with
+the fake pointers used here.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvkv.h")
+
+OK, INVAL, UNSUP, LAUNCH, WS = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_paged_kv_amd import _lib
+    return _lib
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"NVKV_API\s+[\w\s\*]+?\b(\w+)\s*\(", text))
+
+
+def test_every_declared_function_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) == 12, names
+    for n in names:
+        assert hasattr(lib._lib, n), f"{n} not exported by libnvkv.so"
+        assert n in lib.EXPORTED, f"{n} has no binding"
+    assert set(lib.EXPORTED) == names
+
+
+def test_header_is_plain_c():
+    text = open(HEADER).read()
+    assert 'extern "C"' in text and "torch" not in text.lower().replace("torch types", "")
+
+
+def test_status_strings(lib):
+    for st in (OK, INVAL, UNSUP, LAUNCH, WS, 12345):
+        assert isinstance(lib.status_string(st), str) and lib.status_string(st)
+    assert lib.version() >= 100
+
+
+@pytest.mark.parametrize("b,hkv,L,tot", [(4, 8, 131072, 0), (32, 8, 4096, 0), (1, 1, 1, 0), (1, 1, 256, 0),
+                                         (64, 8, 32768, 500000), (44, 8, 8192, 0), (3, 2, 17, 40)])
+def test_plan_covers_the_longest_sequence(lib, b, hkv, L, tot):
+    pps, ns = lib.plan_decode(b, hkv, L, tot)
+    pages = math.ceil(L / 16)
+    assert pps >= 2 and pps % 2 == 0 and ns >= 1
+    assert ns * pps >= pages
+    assert (ns - 1) * pps < pages          # no split starts past the end of the longest sequence
+
+
+def test_plan_forced_split(lib):
+    assert lib.plan_decode(2, 2, 1000, 0, 6) == (6, math.ceil(63 / 6))
+    assert lib.plan_decode(2, 2, 1000, 0, 5) == (6, math.ceil(63 / 6))      # rounded up to even
+    assert lib.plan_decode(2, 2, 100, 0, 1000) == (8, 1)                     # capped at the sequence
+
+
+def test_plan_rejects_bad_hints(lib):
+    for args in ((0, 8, 10, 0, 0), (1, 0, 10, 0, 0), (1, 8, 0, 0, 0), (1, 8, 10, -1, 0), (1, 8, 10, 0, -2)):
+        with pytest.raises(RuntimeError):
+            lib.plan_decode(*args)
+
+
+def test_workspace_size(lib):
+    assert lib.decode_workspace_size(4, 64, 8, 1) == 0
+    n = lib.decode_workspace_size(4, 64, 8, 16)
+    assert n == 4 * 64 * 16 * 130 * 4
+    assert lib._lib.nvkv_decode_workspace_size(4, 64, 8, 64, 16) == 0      # head_dim other than 128
+
+
+# ---- validation of the compute entry points, with fake (never dereferenced) pointers ----
+A = 1 << 20          # a 16-byte aligned fake address
+MIS = A + 4          # misaligned
+S = None             # default stream
+
+
+def _decode(lib, **kw):
+    a = dict(q=A, kd=A, ks=A, vd=A, vs=A, gk=1.0, gv=1.0, pt=A, maxp=4, sl=A, b=1, hq=8, hkv=2, d=128, page=16,
+             sm=0.1, pps=2, ns=1, nk=None, nv=None, out=A, ws=None, wsb=0)
+    a.update(kw)
+    return lib._lib.nvfp4_paged_decode_attn(a["q"], a["kd"], a["ks"], a["vd"], a["vs"], a["gk"], a["gv"], a["pt"],
+                                            a["maxp"], a["sl"], a["b"], a["hq"], a["hkv"], a["d"], a["page"], a["sm"],
+                                            a["pps"], a["ns"], a["nk"], a["nv"], a["out"], a["ws"], a["wsb"], S)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVAL), (dict(kd=None), INVAL), (dict(out=None), INVAL), (dict(pt=None), INVAL),
+    (dict(q=MIS), INVAL), (dict(vs=MIS), INVAL), (dict(out=MIS), INVAL), (dict(sl=A + 2), INVAL),
+    (dict(d=64), UNSUP), (dict(page=32), UNSUP), (dict(d=0), INVAL),
+    (dict(hq=7), INVAL), (dict(hq=64, hkv=2), UNSUP), (dict(hkv=0), INVAL),
+    (dict(gk=float("nan")), INVAL), (dict(gv=0.0), INVAL), (dict(gk=-1.0), INVAL), (dict(gk=float("inf")), INVAL),
+    (dict(sm=0.0), INVAL), (dict(sm=float("nan")), INVAL),
+    (dict(b=0), INVAL), (dict(maxp=0), INVAL), (dict(pps=0), INVAL), (dict(ns=0), INVAL),
+    (dict(nk=A), INVAL),                                    # new_k without new_v
+    (dict(ns=4), WS), (dict(ns=4, ws=A, wsb=100), WS),     # workspace missing / too small
+])
+def test_decode_validation(lib, kw, want):
+    assert _decode(lib, **kw) == want
+
+
+def test_fp8_decode_and_layers_validation(lib):
+    f = lib._lib.fp8_paged_decode_attn
+    assert f(A, A, A, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, None, None, 0, S) == INVAL   # out null
+    assert f(A, A, None, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, None, 0, S) == INVAL
+    assert f(A, A, A, 0.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, None, 0, S) == INVAL
+    assert lib._lib.nvkv_decode_layers(None, 1, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, None, 0, S) == INVAL
+    layers = (lib.NvkvLayer * 2)()
+    layers[0] = lib.NvkvLayer(0, A, A, A, A, A, 1.0, 1.0, A)
+    layers[1] = lib.NvkvLayer(7, A, A, A, A, A, 1.0, 1.0, A)          # unknown precision: nothing launches
+    assert lib._lib.nvkv_decode_layers(ctypes.cast(layers, ctypes.c_void_p), 2, A, 4, A, 1, 8, 2, 128, 16, 0.1,
+                                       2, 1, None, 0, S) == INVAL
+    layers[1] = lib.NvkvLayer(0, A, A, None, A, A, 1.0, 1.0, A)       # NVFP4 layer without K scales
+    assert lib._lib.nvkv_decode_layers(ctypes.cast(layers, ctypes.c_void_p), 2, A, 4, A, 1, 8, 2, 128, 16, 0.1,
+                                       2, 1, None, 0, S) == INVAL
+
+
+def test_quantize_validation(lib):
+    q = lib._lib.nvfp4_kv_quantize_append
+    base = [A, A, 0, 1.0, 1.0, A, 4, 2, 128, 16, 1.0, 1.0, A, A, A, A, S]
+
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return q(*a)
+    assert call(a0=None) == INVAL
+    assert call(a0=MIS) == INVAL
+    assert call(a2=5) == INVAL                           # unknown input dtype
+    assert call(a2=1, a3=0.0) == INVAL                   # FP8 input needs its scale
+    assert call(a6=-1) == INVAL
+    assert call(a6=0) == OK                              # nothing to do: no launch
+    assert call(a8=64) == UNSUP
+    assert call(a9=8) == UNSUP
+    assert call(a10=float("nan")) == INVAL
+    assert call(a11=1e-39) == INVAL                      # subnormal global scale
+    assert call(a15=MIS) == INVAL
+    f = lib._lib.fp8_kv_quantize_append
+    assert f(A, A, A, 4, 2, 128, 16, 0.0, 1.0, A, A, S) == INVAL
+    assert f(A, None, A, 4, 2, 128, 16, 1.0, 1.0, A, A, S) == INVAL
+    assert f(A, A, A, 0, 2, 128, 16, 1.0, 1.0, A, A, S) == OK
+
+
+def test_global_scale_and_dequant_validation(lib):
+    g = lib._lib.nvkv_global_scale
+    wsz = lib._lib.nvkv_global_scale_workspace_size()
+    assert wsz >= 4
+    assert g(A, 0, 1.0, 0, 2688.0, A, A, wsz, S) == INVAL        # empty tensor
+    assert g(A, 0, 1.0, 10, 0.0, A, A, wsz, S) == INVAL          # divisor
+    assert g(A, 2, 1.0, 10, 2688.0, A, A, wsz, S) == INVAL       # dtype
+    assert g(A, 0, 1.0, 10, 2688.0, A, A, wsz - 1, S) == WS
+    assert g(MIS, 0, 1.0, 10, 2688.0, A, A, wsz, S) == INVAL
+    d = lib._lib.nvfp4_dequant_to_workspace
+    args = [A, A, A, A, 1.0, 1.0, A, 4, A, A, 1, 2, 128, 16, 64, 1.0, 1.0, A, A, S]
+    bad = list(args); bad[14] = 65                               # prefix longer than the page table
+    assert d(*bad) == INVAL
+    bad = list(args); bad[15] = 0.0
+    assert d(*bad) == INVAL
+    bad = list(args); bad[17] = None
+    assert d(*bad) == INVAL
+    bad = list(args); bad[12] = 256
+    assert d(*bad) == UNSUP
+    ok0 = list(args); ok0[14] = 0                                 # nothing to gather: no launch
+    assert d(*ok0) == OK

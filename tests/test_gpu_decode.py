@@ -217,3 +217,16 @@ def test_full_size_ragged_fused_sampled(nv):
     longest = int(np.argmax(wl.seq_lens))
     shortest = int(np.argmin(wl.seq_lens))
     _sampled_full_size(nv, 3, [(longest, 2), (shortest, 5)])
+
+
+def test_workspace_reused_across_plans(nv, ragged):
+    wl, pool, gk, gv, want = ragged
+    pt, sl = H.gpu_tables(wl, DEV)
+    q = wl.q().to(DEV)
+    plans = [nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), 0, p) for p in (2, 8, 4, 2)]
+    most = max(p[1] for p in plans)
+    ws = nv.alloc_decode_workspace(wl.batch, wl.h_q, wl.h_kv, most, DEV)
+    for plan in plans:
+        got = nv.nvfp4_decode(q, pool, float(gk), float(gv), pt, sl, wl.sm_scale, plan, wl.h_kv, workspace=ws)
+        torch.cuda.synchronize()
+        H.assert_attention_close(got.cpu().numpy(), want, f"reused workspace plan={plan}")
