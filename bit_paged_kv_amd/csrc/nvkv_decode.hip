@@ -57,21 +57,34 @@ __device__ __forceinline__ void zero_page(PageFp8& p) {
   p.k0 = p.k1 = p.v0 = p.v1 = make_uint4(0, 0, 0, 0);
 }
 
-// blk is wave-uniform and the lane offset an unsigned 32-bit value, so each load is a single
-// global_load with a scalar base and a vector offset (no per-load 64-bit address arithmetic).
+// Raw buffer loads: the page address lives in a scalar buffer resource (built with scalar adds)
+// and each lane supplies only a 32-bit offset, so no vector instruction is spent on addresses.
+// The resource covers exactly one (page, head) block; reads past it return zeros.
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;   // raw (untyped, unswizzled) buffer on gfx9-family GPUs
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, size_t blk, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base) + blk * bytes, 0, bytes, kBufferWord3);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  const u4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// blk is wave-uniform: (page id) * num_kv_heads + head.
 __device__ __forceinline__ void load_page(PageNv4& p, const DecodeArgs& a, size_t blk, unsigned lane) {
-  p.kd = *reinterpret_cast<const uint4*>(a.k_data + blk * kNvfp4DataBytes + lane * 16u);
-  p.ks = *reinterpret_cast<const uint16_t*>(a.k_scale + blk * kNvfp4ScaleBytes + lane * 2u);
-  p.vd = *reinterpret_cast<const uint4*>(a.v_data + blk * kNvfp4DataBytes + lane * 16u);
-  p.vs = *reinterpret_cast<const uint16_t*>(a.v_scale + blk * kNvfp4ScaleBytes + lane * 2u);
+  p.kd = ld16(block_rsrc(a.k_data, blk, kNvfp4DataBytes), lane * 16u);
+  p.ks = __builtin_amdgcn_raw_buffer_load_b16(block_rsrc(a.k_scale, blk, kNvfp4ScaleBytes), lane * 2u, 0, 0);
+  p.vd = ld16(block_rsrc(a.v_data, blk, kNvfp4DataBytes), lane * 16u);
+  p.vs = __builtin_amdgcn_raw_buffer_load_b16(block_rsrc(a.v_scale, blk, kNvfp4ScaleBytes), lane * 2u, 0, 0);
 }
 __device__ __forceinline__ void load_page(PageFp8& p, const DecodeArgs& a, size_t blk, unsigned lane) {
-  const uint4* k = reinterpret_cast<const uint4*>(a.k_data + blk * kFp8Bytes + lane * 32u);
-  const uint4* v = reinterpret_cast<const uint4*>(a.v_data + blk * kFp8Bytes + lane * 32u);
-  p.k0 = k[0];
-  p.k1 = k[1];
-  p.v0 = v[0];
-  p.v1 = v[1];
+  const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k_data, blk, kFp8Bytes);
+  const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v_data, blk, kFp8Bytes);
+  p.k0 = ld16(rk, lane * 32u);
+  p.k1 = ld16(rk, lane * 32u + 16u);
+  p.v0 = ld16(rv, lane * 32u);
+  p.v1 = ld16(rv, lane * 32u + 16u);
 }
 
 __device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
@@ -268,13 +281,15 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
     // re-read that hits in cache) and an odd trailing page is masked, so no branch separates a load
     // from its use and the waits on the vector-memory counter stay precise while two pairs are in flight.
     const int npairs = (pg_end - pg_begin + 1) >> 1;
+    // the wave's slice of the page table as a buffer; ids are read with a scalar offset
+    const __amdgpu_buffer_rsrc_t ids_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(pt + pg_begin), 0, (pg_end - pg_begin) * 4, kBufferWord3);
     int vzero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));   // per-lane zero: keeps page-id loads on the vector path
-    const int32_t* ptw = pt + pg_begin + vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));   // per-lane zero offset: keeps these on the vector path
     auto load_ids = [&](int pair, int& i0, int& i1) {
       const int rel = 2 * min(pair, npairs - 1);
-      i0 = ptw[rel];
-      i1 = ptw[min(rel + 1, pg_end - pg_begin - 1)];
+      i0 = (int)__builtin_amdgcn_raw_buffer_load_b32(ids_rsrc, vzero, rel * 4, 0);
+      i1 = (int)__builtin_amdgcn_raw_buffer_load_b32(ids_rsrc, vzero, min(rel + 1, pg_end - pg_begin - 1) * 4, 0);
     };
     auto issue = [&](Page& p0, Page& p1, int i0, int i1) {
       load_page(p0, a, (size_t)__builtin_amdgcn_readfirstlane(i0) * a.hkv + hk, (unsigned)lane);
@@ -329,12 +344,16 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
 #pragma unroll
       for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk_scale, -m_new));
       l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-      h8 ph, pl;
+      // P = hi + lo in fp16: hi rounds toward zero, lo = P - hi is exact in fp32 and keeps ~11 more bits
+      h2 ph2[4], pl2[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ph[i] = (_Float16)pr[i];
-        pl[i] = (_Float16)(pr[i] - (float)ph[i]);
+      for (int k = 0; k < 4; ++k) {
+        ph2[k] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2 * k], pr[2 * k + 1]));
+        pl2[k] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2 * k] - (float)ph2[k][0],
+                                                                    pr[2 * k + 1] - (float)ph2[k][1]));
       }
+      const h8 ph = cat4(ph2[0], ph2[1], ph2[2], ph2[3]);
+      const h8 pl = cat4(pl2[0], pl2[1], pl2[2], pl2[3]);
       // PV: hi product of block N issued next to the lo product of block N-1
       uint4 vsc0[4], vsc1[4];
       v_scale_pairs(p0, vs_slot, lane, vsc0);
