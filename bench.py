@@ -47,6 +47,49 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+class HipEventPairs:
+    """K pairs of raw hipEvent_t from the HIP runtime the library runs on (timing plumbing only)."""
+
+    def __init__(self, n):
+        import ctypes
+        self._ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")       # the runtime torch has already loaded
+        self.start = [ctypes.c_void_p() for _ in range(n)]
+        self.stop = [ctypes.c_void_p() for _ in range(n)]
+        for e in self.start + self.stop:
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+
+    def elapsed_ms(self):
+        ms = self._ct.c_float()
+        out = []
+        for a, b in zip(self.start, self.stop):
+            if self.hip.hipEventSynchronize(b) != 0 or self.hip.hipEventElapsedTime(self._ct.byref(ms), a, b) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for e in self.start + self.stop:
+            self.hip.hipEventDestroy(e)
+
+
+# HBM traffic of decode_split_kernel on the long workload, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives (x2.000 / x1.000).  Valid only
+# for the kernel source they were taken with; reported as null for any other source.
+TRAFFIC = {
+    "long": {"source_sha256": "57c0c1f463a597ddbe33bacc40dea5b7686eb6a3f06053579fe58fffdf2d6ceb",
+             "fetch_kib": 295380.5, "write_kib": 3273.0, "fetch_factor": 2.0, "write_factor": 1.0},
+}
+
+
+def decode_source_sha256():
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_paged_kv_amd", "csrc", "nvkv_decode.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
 # ------------------------------------------------------------------------------------------------
 def build_layer_cache(nv, wl, layer, dev, fp8=False):
     """Upload one layer's cached K/V and write it into a new pool with the library's kernels."""
@@ -144,10 +187,15 @@ def main():
                                          new_v=new_v, out=out, workspace=ws)[0] for pool in pools]
         counter = [0]
 
-        def step():
-            calls[counter[0] % len(calls)].run()
+        def step(events=None, i=0):
+            call = calls[counter[0] % len(calls)]
+            if events is None:
+                call.run()
+            else:
+                call.run_timed(events.start[i], events.stop[i])
             counter[0] += 1
-        kernel = "decode_split_kernel<PageNv4> + merge_splits_kernel"
+        timed_kernel = "decode_split_kernel<PageNv4>"
+        kernel_bytes = step_bytes
         desc = (f"{name}: batch {wl.batch}, context {int(wl.seq_lens[0]) if name != 'ragged' else 'ragged'}, "
                 f"{wl.h_kv} KV / {wl.h_q} query heads, head_dim 128, page 16, NVFP4 cache, "
                 f"split-K {plan[1]} x {plan[0]} pages")
@@ -173,9 +221,10 @@ def main():
         n_fp8 = len(wl.fp8_layers)
         step_bytes = (wl.layers - n_fp8) * wl.kv_bytes_nvfp4() + n_fp8 * wl.kv_bytes_fp8()
 
-        def step():
+        def step(events=None, i=0):
             nv.decode_layers(layers, pt, sl, wl.sm_scale, plan, wl.h_kv, workspace=ws)
-        kernel = "28 x (decode_split_kernel + merge_splits_kernel)"
+        timed_kernel = None
+        kernel_bytes = None
         desc = (f"mixed: 28 layers (FP8 at {list(wl.fp8_layers)}), batch {wl.batch}, context 8192, "
                 f"8 KV / 32 query heads, split-K {plan[1]} x {plan[0]} pages")
         extra = {"batch": wl.batch, "context_tokens": int(wl.total_lens.sum()), "layers": wl.layers,
@@ -206,7 +255,7 @@ def main():
         k_ws = torch.empty((prefix + chunk, wl.h_kv, 128), dtype=torch.uint8, device=dev)   # shared by layers
         v_ws = torch.empty_like(k_ws)
 
-        def step():
+        def step(events=None, i=0):
             for pool, gk_l, gv_l, ck, cv in caches:
                 nv.dequant_to_workspace(pool, gk_l, gv_l, pt, prefix_lens, offs, prefix, 6.0 * gk_l, 6.0 * gv_l,
                                         wl.h_kv, k_ws, v_ws)
@@ -214,7 +263,8 @@ def main():
         # bytes: read prefix NVFP4 (144 B/token/head), write FP8 workspace (256 B), read chunk bf16 (512 B),
         # write chunk NVFP4 (144 B)
         step_bytes = len(caches) * wl.h_kv * (prefix * (144 + 256) + chunk * (512 + 144))
-        kernel = "24 x (nvfp4_to_fp8_ws_kernel + nvfp4_quantize_kernel)"
+        timed_kernel = None
+        kernel_bytes = None
         desc = (f"extend: {len(caches)} NVFP4 layers x (16384-token prefix -> shared FP8 workspace + "
                 f"2048-token chunk quantize-append), 8 KV heads")
         extra = {"layers": len(caches), "prefix": prefix, "chunk": chunk, "kv_heads": wl.h_kv}
@@ -224,31 +274,57 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the split kernel's own dispatch records one event pair per step (no commands are added to
+    # the stream); the step as a whole is bracketed by device synchronisations
+    events = HipEventPairs(args.steps) if timed_kernel else None
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        step()
+        step(events, i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1) / args.steps     # HIP events on the launch stream, per step
+    step_gpu_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
-    achieved = step_bytes / (gpu_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    if timed_kernel:
+        kms = events.elapsed_ms()
+        events.close()
+        kernel_ms = sum(kms) / len(kms)
+        achieved = kernel_bytes / (kernel_ms * 1e-3) / 1e9
+        timing = (f"{timed_kernel}: mean of {len(kms)} per-launch durations (min {min(kms) * 1e3:.1f} us, max "
+                  f"{max(kms) * 1e3:.1f} us) from hipEvents its dispatch recorded on the launch stream")
+    else:
+        kernel_ms = step_gpu_ms
+        achieved = step_bytes / (kernel_ms * 1e-3) / 1e9
+        timed_kernel = "whole step"
+        timing = "HIP events on the launch stream around the K timed steps, divided by K"
     if name in ("long", "batch32", "tiny", "ragged"):
         assert torch.isfinite(out).all().item(), "non-finite decode output"
-    log(f"{args.steps} steps: wall {ms_per_step:.4f} ms/step, events {gpu_ms:.4f} ms/step, "
-        f"{achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+    log(f"{args.steps} steps: wall {ms_per_step:.4f} ms/step, events {step_gpu_ms:.4f} ms/step, "
+        f"{value:.1f} GB/s ({value / HBM_PEAK_GBS:.1%} of 8 TB/s); {timed_kernel} {kernel_ms * 1e3:.1f} us "
+        f"-> {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")
 
     cpu = None
     if not args.no_cpu_baseline and name in ("long", "batch32", "ragged", "tiny"):
         cpu = cpu_baseline(wl)
         log(f"cpu baseline {cpu['value']} GB/s")
 
-    traffic = None
+    traffic, traffic_detail = None, None
+    t = TRAFFIC.get(name)
+    if t is not None and timed_kernel.startswith("decode_split_kernel"):
+        if decode_source_sha256() == t["source_sha256"]:
+            rd = t["fetch_kib"] * 1024 * t["fetch_factor"]
+            wr = t["write_kib"] * 1024 * t["write_factor"]
+            traffic = round(rd + wr)
+            traffic_detail = {"read_bytes": round(rd), "write_bytes": round(wr),
+                              "algorithmic_read_bytes": kernel_bytes,
+                              "source": "rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE per dispatch x copy calibration"}
+        else:
+            traffic_detail = "kernel source changed since the counters were taken"
     res = {
         "metric": "NVFP4 paged decode attn: effective KV GB/s (% of HBM peak) + tokens/s",
         "value": round(value, 2),
@@ -267,8 +343,9 @@ def main():
         "tokens_per_s": round(tokens_per_step / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
-                     "timing": "HIP events on the launch stream around the K timed steps, divided by K"},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": timed_kernel,
+                     "kernel_us": round(kernel_ms * 1e3, 2), "bytes_per_launch": kernel_bytes or step_bytes,
+                     "traffic_detail": traffic_detail, "timing": timing},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -48,6 +48,8 @@ EXPORTED = {
     "nvkv_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "nvfp4_paged_decode_attn": (_i, [_p, _p, _p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i,
                                      _p, _p, _p, _p, _sz, _p]),
+    "nvfp4_paged_decode_attn_timed": (_i, [_p, _p, _p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i,
+                                           _p, _p, _p, _p, _sz, _p, _p, _p]),
     "fp8_paged_decode_attn": (_i, [_p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p, _p, _sz, _p]),
     "nvkv_decode_layers": (_i, [_p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p, _sz, _p]),
     "nvfp4_dequant_to_workspace": (_i, [_p, _p, _p, _p, _f, _f, _p, _i, _p, _p, _i, _i, _i, _i, _i, _f, _f, _p, _p,
@@ -188,9 +190,10 @@ def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, num_s
 
 
 def alloc_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, num_splits: int, device):
-    """Workspace for decode partials (uninitialised: the kernels write before they read)."""
+    """Workspace for decode: split partials plus per-stream work counters.  Zero-filled here once;
+    every decode call leaves the counters at zero, so it can be reused across calls and plans."""
     n = decode_workspace_size(batch, num_q_heads, num_kv_heads, num_splits)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def _decode_prep(q, page_table, seq_lens, plan, out, workspace, num_kv_heads):
@@ -207,7 +210,7 @@ def _decode_prep(q, page_table, seq_lens, plan, out, workspace, num_kv_heads):
         out = torch.empty((b, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
     need = decode_workspace_size(b, hq, num_kv_heads, ns)
-    if workspace is None and need > 0:
+    if workspace is None:
         workspace = alloc_decode_workspace(b, hq, num_kv_heads, ns, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return b, hq, pps, ns, out, workspace, ws_bytes
@@ -245,6 +248,13 @@ class PreparedDecode:
         st = self._fn(*self._args[:-1], _stream(self._stream_of))
         if st != 0:
             _check(self._fn.__name__, st)
+
+    def run_timed(self, start, stop):
+        """Same call through nvfp4_paged_decode_attn_timed: the split kernel's dispatch records the
+        raw hipEvent_t handles ``start`` / ``stop`` (ints or c_void_p)."""
+        st = _lib.nvfp4_paged_decode_attn_timed(*self._args[:-1], _stream(self._stream_of), start, stop)
+        if st != 0:
+            _check("nvfp4_paged_decode_attn_timed", st)
 
 
 def prepare_nvfp4_decode(q, pool, k_gscale, v_gscale, page_table, seq_lens, sm_scale, plan, num_kv_heads,

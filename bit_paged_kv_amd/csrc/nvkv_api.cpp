@@ -70,6 +70,7 @@ int decode_common_status(const void* q, const int32_t* page_table, int max_pages
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4)) return NVKV_E_INVAL;
   if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return NVKV_E_INVAL;
   if (pages_per_split < 1 || num_splits < 1) return NVKV_E_INVAL;
+  if ((long long)num_splits * batch * num_kv_heads > 0x7FFFFFFFLL) return NVKV_E_INVAL;   // one grid axis
   const size_t need = nvkv::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVKV_E_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return NVKV_E_INVAL;
@@ -183,6 +184,20 @@ int nvfp4_paged_decode_attn(const void* q, const uint8_t* k_data, const uint8_t*
                             int num_q_heads, int num_kv_heads, int head_dim, int page_size, float sm_scale,
                             int pages_per_split, int num_splits, const void* new_k, const void* new_v, float* out,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return nvfp4_paged_decode_attn_timed(q, k_data, k_scale, v_data, v_scale, k_global_scale, v_global_scale,
+                                       page_table, max_pages_per_seq, seq_lens, batch, num_q_heads, num_kv_heads,
+                                       head_dim, page_size, sm_scale, pages_per_split, num_splits, new_k, new_v, out,
+                                       workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int nvfp4_paged_decode_attn_timed(const void* q, const uint8_t* k_data, const uint8_t* k_scale,
+                                  const uint8_t* v_data, const uint8_t* v_scale, float k_global_scale,
+                                  float v_global_scale, const int32_t* page_table, int max_pages_per_seq,
+                                  const int32_t* seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int page_size, float sm_scale, int pages_per_split, int num_splits,
+                                  const void* new_k, const void* new_v, float* out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream, hipEvent_t split_start,
+                                  hipEvent_t split_stop) {
   int st = decode_common_status(q, page_table, max_pages_per_seq, seq_lens, batch, num_q_heads, num_kv_heads,
                                 head_dim, page_size, sm_scale, pages_per_split, num_splits, out, workspace,
                                 workspace_bytes);
@@ -215,7 +230,7 @@ int nvfp4_paged_decode_attn(const void* q, const uint8_t* k_data, const uint8_t*
   a.new_v = new_v;
   a.out = out;
   a.workspace = workspace;
-  return launch_status(nvkv::launch_decode(a, stream));
+  return launch_status(nvkv::launch_decode(a, stream, split_start, split_stop));
 }
 
 int fp8_paged_decode_attn(const void* q, const uint8_t* k_cache, const uint8_t* v_cache, float k_scale, float v_scale,

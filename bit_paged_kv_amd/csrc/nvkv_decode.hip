@@ -20,6 +20,8 @@
 #include <type_traits>
 #include <utility>
 
+#include <hip/hip_ext.h>
+
 #include "nvkv_device.h"
 #include "nvkv_launch.h"
 
@@ -124,42 +126,35 @@ __device__ __forceinline__ h2 k_scales(const PageNv4& p) { return fp8x2_to_h2<fa
 __device__ __forceinline__ h2 k_scales(const PageFp8&) { return h2{(_Float16)1.0f, (_Float16)1.0f}; }
 
 // --- V operands: A[channel 16N + lane%16][k], k = tokens 4*(lane/16)+0..3 of page 0, then page 1 ---
-// sc0 / sc1: the 16 fp16 scale pairs of this lane's token quad (dword 2n + h = tokens +2h, +2h+1 of
-// block n) for page 0 / page 1, gathered through LDS (v_scale_pairs below).
+// q0 / q1: this lane's token quad in the LDS slot of page 0 / page 1 (16 fp16 scale pairs; dword
+// 2n + h = tokens +2h, +2h+1 of block n), written by v_scale_publish below.  Each block's two
+// dwords are read right where they are used, which keeps few of them live.
 template <int N>
-__device__ __forceinline__ h8 v_operand(const PageNv4& p0, const PageNv4& p1, const uint4 (&sc0)[4],
-                                        const uint4 (&sc1)[4]) {
+__device__ __forceinline__ h8 v_operand(const PageNv4& p0, const PageNv4& p1, const uint32_t* q0,
+                                        const uint32_t* q1) {
   constexpr int W = N >> 1;           // dword holding block N
   constexpr int B0 = 2 * (N & 1);     // byte of tokens (+0,+1); B0 + 1 holds tokens (+2,+3)
   const uint32_t d0 = u4get(p0.vd, W), d1 = u4get(p1.vd, W);
-  const h2 s00 = __builtin_bit_cast(h2, u4get(sc0[N >> 1], 2 * (N & 1)));
-  const h2 s01 = __builtin_bit_cast(h2, u4get(sc0[N >> 1], 2 * (N & 1) + 1));
-  const h2 s10 = __builtin_bit_cast(h2, u4get(sc1[N >> 1], 2 * (N & 1)));
-  const h2 s11 = __builtin_bit_cast(h2, u4get(sc1[N >> 1], 2 * (N & 1) + 1));
-  return cat4(fp4x2_to_h2<B0>(d0) * s00, fp4x2_to_h2<B0 + 1>(d0) * s01,
-              fp4x2_to_h2<B0>(d1) * s10, fp4x2_to_h2<B0 + 1>(d1) * s11);
+  const uint2 a = *reinterpret_cast<const uint2*>(q0 + 2 * N);
+  const uint2 b = *reinterpret_cast<const uint2*>(q1 + 2 * N);
+  return cat4(fp4x2_to_h2<B0>(d0) * __builtin_bit_cast(h2, a.x), fp4x2_to_h2<B0 + 1>(d0) * __builtin_bit_cast(h2, a.y),
+              fp4x2_to_h2<B0>(d1) * __builtin_bit_cast(h2, b.x), fp4x2_to_h2<B0 + 1>(d1) * __builtin_bit_cast(h2, b.y));
 }
 template <int N>
-__device__ __forceinline__ h8 v_operand(const PageFp8& p0, const PageFp8& p1, const uint4 (&)[4],
-                                        const uint4 (&)[4]) {
+__device__ __forceinline__ h8 v_operand(const PageFp8& p0, const PageFp8& p1, const uint32_t*, const uint32_t*) {
   const uint32_t a = (N < 4) ? u4get(p0.v0, N & 3) : u4get(p0.v1, N & 3);
   const uint32_t b = (N < 4) ? u4get(p1.v0, N & 3) : u4get(p1.v1, N & 3);
   return cat4(fp8x2_to_h2<false>(a), fp8x2_to_h2<true>(a), fp8x2_to_h2<false>(b), fp8x2_to_h2<true>(b));
 }
 
 // Each lane converts the E4M3 pair it loaded (tokens 4c + 2(lane%2) + {0,1} of block (lane%16)/2)
-// and the 16 lanes of a token quad c exchange their pairs through this wave's LDS slot: lane c*16+x
-// reads back the 16 pairs of quad c in (block, half) order.  LDS operations of one wave complete in
-// order, so no barrier is needed.
-__device__ __forceinline__ void v_scale_pairs(const PageNv4& p, uint32_t* slot, int lane, uint4 (&out)[4]) {
+// and publishes it in this wave's LDS slot, where the 16 lanes of token quad c read the 16 pairs of
+// the quad in (block, half) order.  LDS operations of one wave complete in order, so no barrier is
+// needed.
+__device__ __forceinline__ void v_scale_publish(const PageNv4& p, uint32_t* slot, int lane) {
   slot[lane] = __builtin_bit_cast(uint32_t, fp8x2_to_h2<false>(p.vs));
-  const uint4* src = reinterpret_cast<const uint4*>(slot + 16 * (lane >> 4));
-  out[0] = src[0];
-  out[1] = src[1];
-  out[2] = src[2];
-  out[3] = src[3];
 }
-__device__ __forceinline__ void v_scale_pairs(const PageFp8&, uint32_t*, int, uint4 (&)[4]) {}
+__device__ __forceinline__ void v_scale_publish(const PageFp8&, uint32_t*, int) {}
 
 // Fused quantize-append of one new token (position pos) of kv head hk into the NVFP4 pools.
 // Lanes 0..31 handle K, 32..63 V; four lanes share a 16-channel block (4 channels each).
@@ -201,14 +196,79 @@ __device__ void append_token_nvfp4(const DecodeArgs& a, int b, int hk, int pos, 
   }
 }
 
-// Workspace of a multi-split decode: per (row = b * Hq + h, split) the unnormalised partial output
-// [128] (times g_V), then per (row, split) its (max, sum) in log2 units.
-template <typename Page>
+// Cross-lane partners without an LDS round trip: the gfx950 lane-swap instructions pair lane l with
+// l ^ 16 (permlane16_swap) or l ^ 32 (permlane32_swap).  With both inputs equal, each lane of a pair
+// receives the two values in the same order, so both compute bit-identical results.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// The value lane l ^ 8 holds (same row of 16 lanes): DPP rotation of the row by 8.
+__device__ __forceinline__ float from_lane_xor8(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x128, 0xF, 0xF, false));
+}
+
+// fp16 of (p - hi) for a pair of values with a single rounding (mixed-precision fma): hi + lo then
+// carries about 22 significant bits of p.
+__device__ __forceinline__ h2 lo_part(float p0, float p1, h2 hi) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(r)
+      : "v"(p0), "v"(p1), "v"(hi));
+  return __builtin_bit_cast(h2, r);
+}
+
+// Softmax weights may grow to 2^kSlack (log2 units) above the running maximum before it is raised,
+// so the cross-lane maximum is needed only in the rare pairs that raise it.
+constexpr float kSlack = 8.0f;
+
+// Lane index computed where it is used: the masking of a partial page runs once per wave, and
+// values derived from a loop-invariant lane index would otherwise stay in registers all loop long.
+__device__ __forceinline__ int opaque_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Workspace of a decode: first one 64-byte block of counters per (sequence, kv head) stream (256-byte
+// aligned in total), then per (row = b * Hq + h, split) the unnormalised partial output [128]
+// (times g_V), then per (row, split) its (max, sum) in log2 units.  The counters come first so that
+// their place does not depend on the split count.  Every call leaves them at zero.
+constexpr int kCounterStride = 16;   // uint32 per stream
+
+__host__ __device__ inline size_t counters_bytes(int batch, int hkv) {
+  return (((size_t)batch * hkv * kCounterStride * sizeof(unsigned)) + 255) & ~(size_t)255;
+}
+
+// One workgroup of four waves per (sequence, kv head, split).
+//
+// kPack (query heads per kv head <= 8): score columns 8..15 repeat heads 0..7, and those lanes feed
+// the low fp16 part of P into the PV product while columns 0..7 feed the high part, so one MFMA per
+// 16 channels accumulates both; the two halves of the output are added once at the end.
+template <typename Page, bool kPack>
 __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x;
-  const int hk = blockIdx.y, b = blockIdx.z;
+  // Workgroup order: split-major with the stream index rotated by the split, so that the splits of
+  // a (sequence, kv head) stream are spread over the dispatch order and over the XCDs.
+  const int n_streams = a.batch * a.hkv;
+  const int split = (int)(blockIdx.x / (unsigned)n_streams);
+  const int stream = (int)((blockIdx.x - (unsigned)split * n_streams + (unsigned)(n_streams - split % n_streams)) %
+                           (unsigned)n_streams);
+  const int b = stream / a.hkv, hk = stream - b * a.hkv;
   const int group = a.hq / a.hkv;
   const int seq_len = a.seq_lens[b];
   const int n_pages = (seq_len + kPageSize - 1) / kPageSize;
@@ -220,7 +280,9 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
   const int pg_begin = min(wg_end, wg_begin + wave * quarter);
   const int pg_end = min(wg_end, pg_begin + quarter);
   const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
-  const int jh = lane & 15, c = lane >> 4;
+  const int col = lane & 15, c = lane >> 4;
+  const int jh = kPack ? (col & 7) : col;          // query head (within the group) of this lane's column
+  const bool lo_lane = kPack && col >= 8;          // packed: this column carries the low part of P
   __shared__ uint32_t vs_lds[kWaves][128];                  // per-wave exchange slot for V scale pairs
   __shared__ float red_o[kWaves][16][kHeadDim];             // per-wave partial outputs
   __shared__ float red_ml[kWaves][16][2];                   // per-wave (max, sum) per query head
@@ -261,8 +323,8 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
     float qmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qf[i]));
-    qmax = wave_max_xor(qmax, 16);
-    qmax = wave_max_xor(qmax, 32);
+    qmax = max_xor16(qmax);
+    qmax = max_xor32(qmax);
     int qexp = 0;
     if (qmax > 0.0f) {
       int ex;
@@ -276,6 +338,7 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
       for (int i = 0; i < 8; ++i) qb[s][i] = (_Float16)__builtin_ldexpf(qf[8 * s + i], qexp);
     // scores in log2 units: <q, K_hat> * sm_scale * log2(e); K_hat = (e2m1 * s_blk) * g_K
     const float qk_scale = a.sm_scale * 1.44269504088896341f * a.k_gscale * __builtin_ldexpf(1.0f, -qexp);
+    float thr = -INFINITY;    // raw score above which the running maximum must be raised
 
     // Every load below is unconditional: a pair index past the end is clamped to the last pair (a
     // re-read that hits in cache) and an odd trailing page is masked, so no branch separates a load
@@ -296,19 +359,19 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
       load_page(p1, a, (size_t)__builtin_amdgcn_readfirstlane(i1) * a.hkv + hk, (unsigned)lane);
     };
 
-    // One pair of pages: S^T = K_hat q^T, online softmax, O^T += V_hat^T P^T.  Only the last pair of
-    // a wave's range can hold a partly filled or missing page (tail): masking runs only there.
-    auto process = [&](Page& p0, Page& p1, int pair, bool tail) {
+    // S^T = K_hat q^T for one pair of pages (two independent MFMA chains).  Only the last pair of a
+    // wave's range can hold a partly filled or missing page (tail): masking runs only there.
+    auto scores = [&](Page& p0, Page& p1, int pair, bool tail, float (&x)[8]) {
       const int pg = pg_begin + 2 * pair;
       int nv0 = kPageSize, nv1 = kPageSize;
       if (tail) {
         asm volatile("" ::: "memory");   // keep this a branch: the masking must not run on every pair
         nv0 = min(kPageSize, seq_len - pg * kPageSize);
         nv1 = (pg + 1 < pg_end) ? min(kPageSize, seq_len - (pg + 1) * kPageSize) : 0;
-        if (nv0 < kPageSize) mask_page(p0, nv0, lane);
-        if (nv1 < kPageSize) mask_page(p1, nv1, lane);   // nv1 == 0: a duplicated page, all masked
+        const int ln = opaque_lane_id();
+        if (nv0 < kPageSize) mask_page(p0, nv0, ln);
+        if (nv1 < kPageSize) mask_page(p1, nv1, ln);   // nv1 == 0: a duplicated page, all masked
       }
-      // two independent MFMA chains (one per page), interleaved
       const h2 sc0 = k_scales(p0), sc1 = k_scales(p1);
       f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<0>(p0, sc0), qb[0], s0, 0, 0, 0);
@@ -319,56 +382,78 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<2>(p1, sc1), qb[2], s1, 0, 0, 0);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p0, sc0), qb[3], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p1, sc1), qb[3], s1, 0, 0, 0);
-      // raw scores; qk_scale > 0, so the maximum can be taken before scaling
-      float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = s0[r];
+        x[4 + r] = s1[r];
+      }
       if (tail) {
         asm volatile("" ::: "memory");
+        const int t0 = 4 * (opaque_lane_id() >> 4);   // first token row of this lane
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (4 * c + r >= nv0) x[r] = -INFINITY;
-          if (4 * c + r >= nv1) x[4 + r] = -INFINITY;
+          if (t0 + r >= nv0) x[r] = -INFINITY;
+          if (t0 + r >= nv1) x[4 + r] = -INFINITY;
         }
       }
-      float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mloc = wave_max_xor(mloc, 16);
-      mloc = wave_max_xor(mloc, 32);
-      const float m_new = fmaxf(m_run, mloc * qk_scale);
-      if (__any(m_new > m_run)) {     // rescale only when some head's running max moved
+    };
+
+    // Online softmax over one pair's raw scores, then O^T += V_hat^T P^T.
+    auto accumulate = [&](const Page& p0, const Page& p1, const float (&x)[8]) {
+      v_scale_publish(p0, vs_slot, lane);
+      v_scale_publish(p1, vs_slot + 64, lane);
+      const uint32_t* vq0 = vs_slot + 16 * c;
+      const uint32_t* vq1 = vs_slot + 64 + 16 * c;
+      const float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      if (__any(xm > thr)) {   // some weight would exceed 2^kSlack: raise every head's running maximum
+        const float hmax = max_xor32(max_xor16(xm));
+        const float m_new = fmaxf(m_run, hmax * qk_scale);   // qk_scale > 0: the max commutes with it
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int n = 0; n < 8; ++n) o[n] *= alpha;
+        m_run = m_new;
+        thr = (m_run + kSlack) / qk_scale;
       }
-      m_run = m_new;
       float pr[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk_scale, -m_new));
+      for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk_scale, -m_run));
       l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-      // P = hi + lo in fp16: hi rounds toward zero, lo = P - hi is exact in fp32 and keeps ~11 more bits
+      // P = hi + lo in fp16: hi rounds toward zero, lo = fp16(P - hi) keeps ~11 more bits
       h2 ph2[4], pl2[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         ph2[k] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2 * k], pr[2 * k + 1]));
-        pl2[k] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2 * k] - (float)ph2[k][0],
-                                                                    pr[2 * k + 1] - (float)ph2[k][1]));
+        pl2[k] = lo_part(pr[2 * k], pr[2 * k + 1], ph2[k]);
       }
-      const h8 ph = cat4(ph2[0], ph2[1], ph2[2], ph2[3]);
-      const h8 pl = cat4(pl2[0], pl2[1], pl2[2], pl2[3]);
-      // PV: hi product of block N issued next to the lo product of block N-1
-      uint4 vsc0[4], vsc1[4];
-      v_scale_pairs(p0, vs_slot, lane, vsc0);
-      v_scale_pairs(p1, vs_slot + 64, lane, vsc1);
-      h8 va_prev;
-      static_for<0, 8>([&](auto nc) {
-        constexpr int N = decltype(nc)::value;
-        const h8 va = v_operand<N>(p0, p1, vsc0, vsc1);
-        o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, o[N], 0, 0, 0);
-        if constexpr (N > 0) o[N - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[N - 1], 0, 0, 0);
-        va_prev = va;
-      });
-      o[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[7], 0, 0, 0);
+      if constexpr (kPack) {
+        h2 pp[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pp[k] = lo_lane ? pl2[k] : ph2[k];
+        const h8 pb = cat4(pp[0], pp[1], pp[2], pp[3]);
+        static_for<0, 8>([&](auto nc) {
+          constexpr int N = decltype(nc)::value;
+          o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<N>(p0, p1, vq0, vq1), pb, o[N], 0, 0, 0);
+        });
+      } else {
+        const h8 ph = cat4(ph2[0], ph2[1], ph2[2], ph2[3]);
+        const h8 pl = cat4(pl2[0], pl2[1], pl2[2], pl2[3]);
+        // hi product of block N issued next to the lo product of block N-1
+        h8 va_prev;
+        static_for<0, 8>([&](auto nc) {
+          constexpr int N = decltype(nc)::value;
+          const h8 va = v_operand<N>(p0, p1, vq0, vq1);
+          o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, o[N], 0, 0, 0);
+          if constexpr (N > 0) o[N - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[N - 1], 0, 0, 0);
+          va_prev = va;
+        });
+        o[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[7], 0, 0, 0);
+      }
     };
 
+    // Software pipeline: the scores of pair p+1 are computed right after pair p's PV products are
+    // issued, so the matrix cores and the next pair's decode overlap the softmax dependency chain.
+    float x[8];
     if constexpr (std::is_same<Page, PageNv4>::value) {
       // Three register buffers in rotation: two pairs are in flight while one is computed; page ids
       // are fetched one pair ahead of the data that needs them.
@@ -379,19 +464,23 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
       load_ids(2, c0, c1);
       issue(pa0, pa1, a0, a1);
       issue(pb0, pb1, b0, b1);
+      scores(pa0, pa1, 0, npairs <= 1, x);
       for (int pr = 0;; pr += 3) {
         load_ids(pr + 3, a0, a1);
         issue(pc0, pc1, c0, c1);
-        process(pa0, pa1, pr, pr + 1 >= npairs);
+        accumulate(pa0, pa1, x);
         if (pr + 1 >= npairs) break;
+        scores(pb0, pb1, pr + 1, pr + 2 >= npairs, x);
         load_ids(pr + 4, b0, b1);
         issue(pa0, pa1, a0, a1);
-        process(pb0, pb1, pr + 1, pr + 2 >= npairs);
+        accumulate(pb0, pb1, x);
         if (pr + 2 >= npairs) break;
+        scores(pc0, pc1, pr + 2, pr + 3 >= npairs, x);
         load_ids(pr + 5, c0, c1);
         issue(pb0, pb1, b0, b1);
-        process(pc0, pc1, pr + 2, pr + 3 >= npairs);
+        accumulate(pc0, pc1, x);
         if (pr + 3 >= npairs) break;
+        scores(pa0, pa1, pr + 3, pr + 4 >= npairs, x);
       }
     } else {
       // FP8 pages take twice the registers: two buffers, one pair in flight while one is computed.
@@ -400,27 +489,37 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
       load_ids(0, a0, a1);
       load_ids(1, b0, b1);
       issue(pa0, pa1, a0, a1);
+      scores(pa0, pa1, 0, npairs <= 1, x);
       for (int pr = 0;; pr += 2) {
         load_ids(pr + 2, a0, a1);
         issue(pb0, pb1, b0, b1);
-        process(pa0, pa1, pr, pr + 1 >= npairs);
+        accumulate(pa0, pa1, x);
         if (pr + 1 >= npairs) break;
+        scores(pb0, pb1, pr + 1, pr + 2 >= npairs, x);
         load_ids(pr + 3, b0, b1);
         issue(pa0, pa1, a0, a1);
-        process(pb0, pb1, pr + 1, pr + 2 >= npairs);
+        accumulate(pb0, pb1, x);
         if (pr + 2 >= npairs) break;
+        scores(pa0, pa1, pr + 2, pr + 3 >= npairs, x);
       }
     }
-    l_run = wave_sum_xor(l_run, 16);
-    l_run = wave_sum_xor(l_run, 32);
+    l_run = sum_xor32(sum_xor16(l_run));
+    if constexpr (kPack) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[n][r] += from_lane_xor8(o[n][r]);
+    }
   }
 
   // ---- combine the 4 waves of this workgroup (lane holds O^T[16n + 4c + r][head jh]) ----
+  if (!lo_lane) {
 #pragma unroll
-  for (int n = 0; n < 8; ++n) *reinterpret_cast<f4*>(&red_o[wave][jh][16 * n + 4 * c]) = o[n];
-  if (c == 0) {
-    red_ml[wave][jh][0] = m_run;
-    red_ml[wave][jh][1] = l_run;
+    for (int n = 0; n < 8; ++n) *reinterpret_cast<f4*>(&red_o[wave][jh][16 * n + 4 * c]) = o[n];
+    if (c == 0) {
+      red_ml[wave][jh][0] = m_run;
+      red_ml[wave][jh][1] = l_run;
+    }
   }
   __syncthreads();
   const int tj = threadIdx.x >> 4;            // query head (within the group) of this thread
@@ -456,7 +555,7 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
   }
 
   // ---- several splits: publish this workgroup's partial for the merge kernel ----
-  float* part_o = reinterpret_cast<float*>(a.workspace);
+  float* part_o = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + counters_bytes(a.batch, a.hkv));
   float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
   if (t_ok) {
     float* dst = part_o + (trow * a.num_splits + split) * kHeadDim + td;
@@ -519,20 +618,30 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restri
 }
 
 size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits) {
-  (void)hkv;
-  if (num_splits <= 1) return 0;
-  return (size_t)batch * hq * num_splits * (kHeadDim + 2) * sizeof(float);
+  const size_t partials = num_splits > 1 ? (size_t)batch * hq * num_splits * (kHeadDim + 2) * sizeof(float) : 0;
+  return counters_bytes(batch, hkv) + partials;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_splits, a.hkv, a.batch);
-  if (a.format == kFmtNvfp4)
-    hipLaunchKernelGGL(decode_split_kernel<PageNv4>, grid, dim3(64 * kWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<PageFp8>, grid, dim3(64 * kWaves), 0, stream, a);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  const dim3 grid((unsigned)a.num_splits * a.batch * a.hkv);
+  // the extended launch lets the dispatch packet itself record the events: no extra stream commands
+  const bool pack = a.hq / a.hkv <= 8;
+  const dim3 block(64 * kWaves);
+  if (a.format == kFmtNvfp4) {
+    if (pack)
+      hipExtLaunchKernelGGL(decode_split_kernel<PageNv4, true>, grid, block, 0, stream, start, stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(decode_split_kernel<PageNv4, false>, grid, block, 0, stream, start, stop, 0, a);
+  } else {
+    if (pack)
+      hipExtLaunchKernelGGL(decode_split_kernel<PageFp8, true>, grid, block, 0, stream, start, stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(decode_split_kernel<PageFp8, false>, grid, block, 0, stream, start, stop, 0, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
-  const float* part_o = reinterpret_cast<const float*>(a.workspace);
+  const float* part_o =
+      reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.workspace) + counters_bytes(a.batch, a.hkv));
   const float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
   hipLaunchKernelGGL(merge_splits_kernel, dim3(a.batch * a.hq), dim3(256), 0, stream, part_o, part_ml, a.num_splits,
                      a.out);

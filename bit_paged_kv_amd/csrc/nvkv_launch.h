@@ -48,6 +48,8 @@ struct DecodeArgs {
 };
 
 size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// start / stop (may be null) are recorded by the split kernel's own dispatch.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start = nullptr,
+                         hipEvent_t stop = nullptr);
 
 }  // namespace nvkv

@@ -122,8 +122,8 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
  * Split planning for decode.  The sequence axis is cut into splits of `pages_per_split` pages;
  * each (sequence, kv head, split) is one workgroup of four wavefronts (each takes a contiguous
  * quarter of the split and the four combine in LDS); with several splits a second kernel merges the
- * partial softmax states.  nvkv_plan_decode picks the split from host-side hints so that the grid
- * fills the GPU:
+ * partial softmax states.
+ * nvkv_plan_decode picks num_splits from host-side hints so that the grid fills the GPU:
  *   max_seq_len  : the longest sequence (tokens, including an appended token), > 0.
  *   total_tokens : sum of sequence lengths if known, else 0 (then batch * max_seq_len is assumed).
  *   force_pages_per_split : > 0 forces the split size (rounded up to even); 0 = automatic.
@@ -134,7 +134,14 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
 NVKV_API int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long total_tokens,
                      int force_pages_per_split, int* pages_per_split, int* num_splits);
 
-/* Workspace bytes for decode with the given plan (0 when num_splits == 1); contents need no init. */
+/*
+ * Workspace bytes for decode with the given plan (never 0).  It holds the per-stream work
+ * counters (64 bytes per (sequence, kv head), padded to 256 bytes) followed by the split partials.
+ * The caller zero-fills a workspace before its first use (e.g. hipMemsetAsync) and again if a
+ * later call has a larger batch * num_kv_heads; every decode call leaves the counters at zero, so
+ * the workspace can be reused by later calls with any plan whose size query is not larger.  Calls
+ * that share a workspace must not overlap in time.
+ */
 NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                            int num_splits);
 
@@ -156,7 +163,7 @@ NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_k
  *                  per sequence at position seq_lens[b] - 1 (its page must be in the page table)
  *                  before attending; uses k_global_scale / v_global_scale.  Both or neither.
  *   out        : [batch][num_q_heads][128] fp32, device.
- *   workspace  : >= nvkv_decode_workspace_size(...) bytes, device (may be NULL if that is 0).
+ *   workspace  : >= nvkv_decode_workspace_size(...) bytes, device, zero-filled before its first use.
  */
 NVKV_API int nvfp4_paged_decode_attn(const void* q,
                             const uint8_t* k_data, const uint8_t* k_scale,
@@ -167,6 +174,24 @@ NVKV_API int nvfp4_paged_decode_attn(const void* q,
                             float sm_scale, int pages_per_split, int num_splits,
                             const void* new_k, const void* new_v,
                             float* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_paged_decode_attn_timed -- nvfp4_paged_decode_attn with a measurement hook: split_start and
+ * split_stop (hipEvent_t created by the caller with default flags, or NULL) are recorded by the
+ * dispatch of the split kernel itself (an extended launch), so hipEventElapsedTime(split_start,
+ * split_stop) is that kernel's execution time and no command is added to the stream.  The merge
+ * kernel, when launched, is not inside the pair.  Arguments, results and errors as above.
+ */
+NVKV_API int nvfp4_paged_decode_attn_timed(const void* q,
+                            const uint8_t* k_data, const uint8_t* k_scale,
+                            const uint8_t* v_data, const uint8_t* v_scale,
+                            float k_global_scale, float v_global_scale,
+                            const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens,
+                            int batch, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                            float sm_scale, int pages_per_split, int num_splits,
+                            const void* new_k, const void* new_v,
+                            float* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            hipEvent_t split_start, hipEvent_t split_stop);
 
 /*
  * fp8_paged_decode_attn -- the same decode step over a per-tensor-scaled FP8 E4M3 cache (the

@@ -30,7 +30,7 @@ def _declared():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib._lib, n), f"{n} not exported by libnvkv.so"
         assert n in lib.EXPORTED, f"{n} has no binding"
@@ -71,9 +71,11 @@ def test_plan_rejects_bad_hints(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.decode_workspace_size(4, 64, 8, 1) == 0
+    counters = 4 * 8 * 64                                                 # 64 B per (sequence, kv head)
+    assert lib.decode_workspace_size(4, 64, 8, 1) == counters             # one split: counters only
     n = lib.decode_workspace_size(4, 64, 8, 16)
-    assert n == 4 * 64 * 16 * 130 * 4
+    assert n == counters + 4 * 64 * 16 * 130 * 4                         # counters, then the partials
+    assert lib.decode_workspace_size(1, 4, 1, 3) == 256 + 1 * 4 * 3 * 130 * 4   # counters padded to 256 B
     assert lib._lib.nvkv_decode_workspace_size(4, 64, 8, 64, 16) == 0      # head_dim other than 128
 
 
@@ -85,7 +87,7 @@ S = None             # default stream
 
 def _decode(lib, **kw):
     a = dict(q=A, kd=A, ks=A, vd=A, vs=A, gk=1.0, gv=1.0, pt=A, maxp=4, sl=A, b=1, hq=8, hkv=2, d=128, page=16,
-             sm=0.1, pps=2, ns=1, nk=None, nv=None, out=A, ws=None, wsb=0)
+             sm=0.1, pps=2, ns=1, nk=None, nv=None, out=A, ws=A, wsb=1 << 20)
     a.update(kw)
     return lib._lib.nvfp4_paged_decode_attn(a["q"], a["kd"], a["ks"], a["vd"], a["vs"], a["gk"], a["gv"], a["pt"],
                                             a["maxp"], a["sl"], a["b"], a["hq"], a["hkv"], a["d"], a["page"], a["sm"],
@@ -101,26 +103,42 @@ def _decode(lib, **kw):
     (dict(sm=0.0), INVAL), (dict(sm=float("nan")), INVAL),
     (dict(b=0), INVAL), (dict(maxp=0), INVAL), (dict(pps=0), INVAL), (dict(ns=0), INVAL),
     (dict(nk=A), INVAL),                                    # new_k without new_v
-    (dict(ns=4), WS), (dict(ns=4, ws=A, wsb=100), WS),     # workspace missing / too small
+    (dict(ns=4, ws=None, wsb=0), WS), (dict(ns=4, wsb=100), WS),   # workspace missing / too small
+    (dict(ns=1, ws=None, wsb=0), WS), (dict(ns=1, wsb=63), WS),    # one split still needs the counters
+    (dict(ws=MIS), INVAL),                                           # misaligned workspace
 ])
 def test_decode_validation(lib, kw, want):
     assert _decode(lib, **kw) == want
 
 
+@pytest.mark.parametrize("kw,want", [(dict(q=None), INVAL), (dict(d=64), UNSUP), (dict(ns=4), WS),
+                                     (dict(ns=1), WS)])
+def test_timed_decode_validates_like_the_plain_call(lib, kw, want):
+    a = dict(q=A, kd=A, ks=A, vd=A, vs=A, gk=1.0, gv=1.0, pt=A, maxp=4, sl=A, b=1, hq=8, hkv=2, d=128, page=16,
+             sm=0.1, pps=2, ns=1, nk=None, nv=None, out=A, ws=None, wsb=0)
+    a.update(kw)
+    st = lib._lib.nvfp4_paged_decode_attn_timed(a["q"], a["kd"], a["ks"], a["vd"], a["vs"], a["gk"], a["gv"],
+                                                a["pt"], a["maxp"], a["sl"], a["b"], a["hq"], a["hkv"], a["d"],
+                                                a["page"], a["sm"], a["pps"], a["ns"], a["nk"], a["nv"], a["out"],
+                                                a["ws"], a["wsb"], S, None, None)
+    assert st == want
+
+
 def test_fp8_decode_and_layers_validation(lib):
     f = lib._lib.fp8_paged_decode_attn
-    assert f(A, A, A, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, None, None, 0, S) == INVAL   # out null
-    assert f(A, A, None, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, None, 0, S) == INVAL
-    assert f(A, A, A, 0.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, None, 0, S) == INVAL
-    assert lib._lib.nvkv_decode_layers(None, 1, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, None, 0, S) == INVAL
+    assert f(A, A, A, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, None, A, 1 << 20, S) == INVAL   # out null
+    assert f(A, A, A, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, None, 0, S) == WS     # no workspace
+    assert f(A, A, None, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, A, 1 << 20, S) == INVAL
+    assert f(A, A, A, 0.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, A, 1 << 20, S) == INVAL
+    assert lib._lib.nvkv_decode_layers(None, 1, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, 1 << 20, S) == INVAL
     layers = (lib.NvkvLayer * 2)()
     layers[0] = lib.NvkvLayer(0, A, A, A, A, A, 1.0, 1.0, A)
     layers[1] = lib.NvkvLayer(7, A, A, A, A, A, 1.0, 1.0, A)          # unknown precision: nothing launches
     assert lib._lib.nvkv_decode_layers(ctypes.cast(layers, ctypes.c_void_p), 2, A, 4, A, 1, 8, 2, 128, 16, 0.1,
-                                       2, 1, None, 0, S) == INVAL
+                                       2, 1, A, 1 << 20, S) == INVAL
     layers[1] = lib.NvkvLayer(0, A, A, None, A, A, 1.0, 1.0, A)       # NVFP4 layer without K scales
     assert lib._lib.nvkv_decode_layers(ctypes.cast(layers, ctypes.c_void_p), 2, A, 4, A, 1, 8, 2, 128, 16, 0.1,
-                                       2, 1, None, 0, S) == INVAL
+                                       2, 1, A, 1 << 20, S) == INVAL
 
 
 def test_quantize_validation(lib):
