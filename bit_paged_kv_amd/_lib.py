@@ -190,10 +190,9 @@ def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, num_s
 
 
 def alloc_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, num_splits: int, device):
-    """Workspace for decode: split partials plus per-stream work counters.  Zero-filled here once;
-    every decode call leaves the counters at zero, so it can be reused across calls and plans."""
+    """Workspace for decode partials (uninitialised: the kernels write before they read)."""
     n = decode_workspace_size(batch, num_q_heads, num_kv_heads, num_splits)
-    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def _decode_prep(q, page_table, seq_lens, plan, out, workspace, num_kv_heads):
@@ -210,7 +209,7 @@ def _decode_prep(q, page_table, seq_lens, plan, out, workspace, num_kv_heads):
         out = torch.empty((b, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
     need = decode_workspace_size(b, hq, num_kv_heads, ns)
-    if workspace is None:
+    if workspace is None and need > 0:
         workspace = alloc_decode_workspace(b, hq, num_kv_heads, ns, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return b, hq, pps, ns, out, workspace, ws_bytes

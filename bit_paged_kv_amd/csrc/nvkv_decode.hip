@@ -243,16 +243,9 @@ __device__ __forceinline__ int opaque_lane_id() {
   return l;
 }
 
-// Workspace of a decode: first one 64-byte block of counters per (sequence, kv head) stream (256-byte
-// aligned in total), then per (row = b * Hq + h, split) the unnormalised partial output [128]
-// (times g_V), then per (row, split) its (max, sum) in log2 units.  The counters come first so that
-// their place does not depend on the split count.  Every call leaves them at zero.
-constexpr int kCounterStride = 16;   // uint32 per stream
-
-__host__ __device__ inline size_t counters_bytes(int batch, int hkv) {
-  return (((size_t)batch * hkv * kCounterStride * sizeof(unsigned)) + 255) & ~(size_t)255;
-}
-
+// Workspace of a multi-split decode: per (row = b * Hq + h, split) the unnormalised partial output
+// [128] (times g_V), then per (row, split) its (max, sum) in log2 units.  Every entry is written
+// before it is read, so the workspace needs no initialisation.
 // One workgroup of four waves per (sequence, kv head, split).
 //
 // kPack (query heads per kv head <= 8): score columns 8..15 repeat heads 0..7, and those lanes feed
@@ -555,7 +548,7 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
   }
 
   // ---- several splits: publish this workgroup's partial for the merge kernel ----
-  float* part_o = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + counters_bytes(a.batch, a.hkv));
+  float* part_o = reinterpret_cast<float*>(a.workspace);
   float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
   if (t_ok) {
     float* dst = part_o + (trow * a.num_splits + split) * kHeadDim + td;
@@ -618,8 +611,8 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restri
 }
 
 size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits) {
-  const size_t partials = num_splits > 1 ? (size_t)batch * hq * num_splits * (kHeadDim + 2) * sizeof(float) : 0;
-  return counters_bytes(batch, hkv) + partials;
+  (void)hkv;
+  return num_splits > 1 ? (size_t)batch * hq * num_splits * (kHeadDim + 2) * sizeof(float) : 0;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
@@ -640,8 +633,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t sta
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
-  const float* part_o =
-      reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.workspace) + counters_bytes(a.batch, a.hkv));
+  const float* part_o = reinterpret_cast<const float*>(a.workspace);
   const float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
   hipLaunchKernelGGL(merge_splits_kernel, dim3(a.batch * a.hq), dim3(256), 0, stream, part_o, part_ml, a.num_splits,
                      a.out);

@@ -134,14 +134,7 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
 NVKV_API int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long total_tokens,
                      int force_pages_per_split, int* pages_per_split, int* num_splits);
 
-/*
- * Workspace bytes for decode with the given plan (never 0).  It holds the per-stream work
- * counters (64 bytes per (sequence, kv head), padded to 256 bytes) followed by the split partials.
- * The caller zero-fills a workspace before its first use (e.g. hipMemsetAsync) and again if a
- * later call has a larger batch * num_kv_heads; every decode call leaves the counters at zero, so
- * the workspace can be reused by later calls with any plan whose size query is not larger.  Calls
- * that share a workspace must not overlap in time.
- */
+/* Workspace bytes for decode with the given plan (0 when num_splits == 1); contents need no init. */
 NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                            int num_splits);
 
@@ -163,7 +156,7 @@ NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_k
  *                  per sequence at position seq_lens[b] - 1 (its page must be in the page table)
  *                  before attending; uses k_global_scale / v_global_scale.  Both or neither.
  *   out        : [batch][num_q_heads][128] fp32, device.
- *   workspace  : >= nvkv_decode_workspace_size(...) bytes, device, zero-filled before its first use.
+ *   workspace  : >= nvkv_decode_workspace_size(...) bytes, device (may be NULL if that is 0).
  */
 NVKV_API int nvfp4_paged_decode_attn(const void* q,
                             const uint8_t* k_data, const uint8_t* k_scale,

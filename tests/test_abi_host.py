@@ -71,11 +71,10 @@ def test_plan_rejects_bad_hints(lib):
 
 
 def test_workspace_size(lib):
-    counters = 4 * 8 * 64                                                 # 64 B per (sequence, kv head)
-    assert lib.decode_workspace_size(4, 64, 8, 1) == counters             # one split: counters only
+    assert lib.decode_workspace_size(4, 64, 8, 1) == 0                   # one split: no partials
     n = lib.decode_workspace_size(4, 64, 8, 16)
-    assert n == counters + 4 * 64 * 16 * 130 * 4                         # counters, then the partials
-    assert lib.decode_workspace_size(1, 4, 1, 3) == 256 + 1 * 4 * 3 * 130 * 4   # counters padded to 256 B
+    assert n == 4 * 64 * 16 * 130 * 4                                    # [row][split][128 + 2] fp32
+    assert lib.decode_workspace_size(1, 4, 1, 3) == 1 * 4 * 3 * 130 * 4
     assert lib._lib.nvkv_decode_workspace_size(4, 64, 8, 64, 16) == 0      # head_dim other than 128
 
 
@@ -104,15 +103,13 @@ def _decode(lib, **kw):
     (dict(b=0), INVAL), (dict(maxp=0), INVAL), (dict(pps=0), INVAL), (dict(ns=0), INVAL),
     (dict(nk=A), INVAL),                                    # new_k without new_v
     (dict(ns=4, ws=None, wsb=0), WS), (dict(ns=4, wsb=100), WS),   # workspace missing / too small
-    (dict(ns=1, ws=None, wsb=0), WS), (dict(ns=1, wsb=63), WS),    # one split still needs the counters
-    (dict(ws=MIS), INVAL),                                           # misaligned workspace
+    (dict(ns=4, ws=MIS, wsb=1 << 20), INVAL),                        # misaligned workspace
 ])
 def test_decode_validation(lib, kw, want):
     assert _decode(lib, **kw) == want
 
 
-@pytest.mark.parametrize("kw,want", [(dict(q=None), INVAL), (dict(d=64), UNSUP), (dict(ns=4), WS),
-                                     (dict(ns=1), WS)])
+@pytest.mark.parametrize("kw,want", [(dict(q=None), INVAL), (dict(d=64), UNSUP), (dict(ns=4), WS)])
 def test_timed_decode_validates_like_the_plain_call(lib, kw, want):
     a = dict(q=A, kd=A, ks=A, vd=A, vs=A, gk=1.0, gv=1.0, pt=A, maxp=4, sl=A, b=1, hq=8, hkv=2, d=128, page=16,
              sm=0.1, pps=2, ns=1, nk=None, nv=None, out=A, ws=None, wsb=0)
@@ -127,7 +124,7 @@ def test_timed_decode_validates_like_the_plain_call(lib, kw, want):
 def test_fp8_decode_and_layers_validation(lib):
     f = lib._lib.fp8_paged_decode_attn
     assert f(A, A, A, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, None, A, 1 << 20, S) == INVAL   # out null
-    assert f(A, A, A, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, None, 0, S) == WS     # no workspace
+    assert f(A, A, A, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 4, A, None, 0, S) == WS     # no workspace
     assert f(A, A, None, 1.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, A, 1 << 20, S) == INVAL
     assert f(A, A, A, 0.0, 1.0, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, A, 1 << 20, S) == INVAL
     assert lib._lib.nvkv_decode_layers(None, 1, A, 4, A, 1, 8, 2, 128, 16, 0.1, 2, 1, A, 1 << 20, S) == INVAL

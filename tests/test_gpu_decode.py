@@ -87,28 +87,24 @@ def test_decode_page_permutation_invariance(nv):
     for wl in (a, b):
         pool, gk, gv = H.gpu_nvfp4_layer(wl, 0, DEV)
         outs.append(_run_nvfp4(nv, wl, pool, gk, gv, force_pps=4)[0])
-    # the same attention up to the order of the fp32 sums: which wave takes which pair of pages is
-    # decided at run time, so the outputs agree to rounding, not bit for bit
-    assert np.abs(outs[0] - outs[1]).max() < 1e-5
+    # the same pages in the same order: the result must not depend on where they sit in the pool
+    assert np.array_equal(outs[0], outs[1])
 
 
 def test_decode_repeat_calls_agree_to_rounding(nv, ragged):
-    """Run-to-run: the work counters are back at zero after each call (a stale counter would skip
-    pages and move the output far beyond rounding)."""
+    """Run-to-run: a shared workspace reused by several calls gives the same result each time."""
     wl, pool, gk, gv, want = ragged
     pt, sl = H.gpu_tables(wl, DEV)
     q = wl.q().to(DEV)
     plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), 0, 2)
-    ws = nv.alloc_decode_workspace(wl.batch, wl.h_q, wl.h_kv, plan[1], DEV)      # zero-filled once
+    ws = nv.alloc_decode_workspace(wl.batch, wl.h_q, wl.h_kv, plan[1], DEV)
     outs = []
     for _ in range(4):
         outs.append(nv.nvfp4_decode(q, pool, float(gk), float(gv), pt, sl, wl.sm_scale, plan, wl.h_kv,
                                     workspace=ws).cpu().numpy())
-    counters = ws[:wl.batch * wl.h_kv * 64].view(torch.int32).cpu()
-    assert int(counters.abs().sum()) == 0, "work counters not returned to zero"
     for o in outs:
         H.assert_attention_close(o, want, "repeat")
-        assert np.abs(o - outs[0]).max() < 1e-5
+        assert np.array_equal(o, outs[0])
 
 
 def test_decode_fused_append(nv):
@@ -273,7 +269,7 @@ def test_timed_entry_matches_and_records_the_split_kernel(nv, ragged):
         out.fill_(float("nan"))
         call.run_timed(ev[0], ev[1])
         torch.cuda.synchronize()
-        assert (out - plain).abs().max().item() < 1e-5     # same call up to the run-time order of sums
+        assert torch.equal(out, plain)
         ms = ctypes.c_float()
         assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
         assert 0.0 < ms.value < 1000.0
