@@ -160,7 +160,10 @@ int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long tot
     const long long seq_pages = total_tokens > 0 ? (total_tokens + (long long)batch * (kPage - 1)) / kPage
                                                  : (long long)batch * max_pages;
     const long long work = seq_pages * num_kv_heads;
-    const long long target = (long long)device_cus() * 3;
+    long long target = (long long)device_cus() * 3;
+    // ragged batch (lengths known to differ): smaller splits, so that the hardware can hand the
+    // splits of short sequences to compute units that finished early
+    if (total_tokens > 0 && total_tokens * 10 < (long long)batch * max_seq_len * 9) target = target * 3 / 2;
     pps = std::max<long long>(8, (work + target - 1) / target);
     pps = (pps + 7) & ~7LL;                             // whole pairs of pages for each of the 4 waves
   }
