@@ -146,9 +146,7 @@ def global_scale(x: torch.Tensor, divisor: float = NVFP4_GLOBAL_DIVISOR, in_scal
 # ------------------------------------------------------------------------------------------------
 # a2 / a5: quantize-on-write
 # ------------------------------------------------------------------------------------------------
-def nvfp4_quantize_append(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, k_gscale: float, v_gscale: float,
-                          pool: dict, k_in_scale: float = 1.0, v_in_scale: float = 1.0):
-    """Quantize k, v ([n_tok][H_kv][128], bf16 or E4M3 bytes) into the NVFP4 pool at `slots` (int32)."""
+def _nvfp4_quantize_args(k, v, slots, k_gscale, v_gscale, pool, k_in_scale, v_in_scale):
     dt = IN_BF16 if k.dtype == torch.bfloat16 else IN_FP8
     _need(k, k.dtype, "k")
     _need(v, k.dtype, "v")
@@ -157,10 +155,22 @@ def nvfp4_quantize_append(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor,
         raise ValueError("k, v must be [n_tok][H_kv][128] and slots [n_tok]")
     for key in ("k_data", "k_scale", "v_data", "v_scale"):
         _need(pool[key], torch.uint8, key)
-    _check("nvfp4_kv_quantize_append", _lib.nvfp4_kv_quantize_append(
-        _ptr(k), _ptr(v), dt, k_in_scale, v_in_scale, _ptr(slots), k.shape[0], k.shape[1], HEAD_DIM, PAGE_SIZE,
-        k_gscale, v_gscale, _ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]), _ptr(pool["v_scale"]),
-        _stream(k)))
+    return (_ptr(k), _ptr(v), dt, k_in_scale, v_in_scale, _ptr(slots), k.shape[0], k.shape[1], HEAD_DIM, PAGE_SIZE,
+            k_gscale, v_gscale, _ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]),
+            _ptr(pool["v_scale"]), None)
+
+
+def nvfp4_quantize_append(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, k_gscale: float, v_gscale: float,
+                          pool: dict, k_in_scale: float = 1.0, v_in_scale: float = 1.0):
+    """Quantize k, v ([n_tok][H_kv][128], bf16 or E4M3 bytes) into the NVFP4 pool at `slots` (int32)."""
+    args = _nvfp4_quantize_args(k, v, slots, k_gscale, v_gscale, pool, k_in_scale, v_in_scale)
+    _check("nvfp4_kv_quantize_append", _lib.nvfp4_kv_quantize_append(*args[:-1], _stream(k)))
+
+
+def prepare_nvfp4_quantize_append(k, v, slots, k_gscale, v_gscale, pool, k_in_scale=1.0, v_in_scale=1.0):
+    """nvfp4_quantize_append validated and marshalled once; ``run()`` re-issues it (same buffers)."""
+    args = _nvfp4_quantize_args(k, v, slots, k_gscale, v_gscale, pool, k_in_scale, v_in_scale)
+    return PreparedCall(_lib.nvfp4_kv_quantize_append, args, (k, v, slots, pool), k)
 
 
 def fp8_quantize_append(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, k_scale: float, v_scale: float,
@@ -230,11 +240,11 @@ def nvfp4_decode(q: torch.Tensor, pool: dict, k_gscale: float, v_gscale: float, 
     return out
 
 
-class PreparedDecode:
-    """A decode call with every argument marshalled once: ``run()`` is a single C call.
+class PreparedCall:
+    """One C call with every argument marshalled once: ``run()`` is a single ctypes call.
 
-    For serving loops that replay the same step (same buffers, same plan) many times; the tensors
-    passed in are kept alive by this object.
+    For loops that replay the same step (same buffers, same sizes) many times; the tensors passed
+    in are kept alive by this object.  The stream is looked up at each ``run()``.
     """
 
     def __init__(self, fn, args, keep, stream_of):
@@ -247,6 +257,10 @@ class PreparedDecode:
         st = self._fn(*self._args[:-1], _stream(self._stream_of))
         if st != 0:
             _check(self._fn.__name__, st)
+
+
+class PreparedDecode(PreparedCall):
+    """A prepared nvfp4_paged_decode_attn call (see PreparedCall) that can also be timed."""
 
     def run_timed(self, start, stop):
         """Same call through nvfp4_paged_decode_attn_timed: the split kernel's dispatch records the
@@ -279,9 +293,7 @@ def fp8_decode(q: torch.Tensor, pool: dict, k_scale: float, v_scale: float, page
     return out
 
 
-def decode_layers(layers: list, page_table: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float, plan,
-                  num_kv_heads: int, workspace=None):
-    """One decode step across layers.  Each entry: dict(precision, q, pool, k_gscale, v_gscale, out)."""
+def _decode_layers_args(layers, page_table, seq_lens, sm_scale, plan, num_kv_heads, workspace):
     if not layers:
         raise ValueError("no layers")
     q0 = layers[0]["q"]
@@ -301,18 +313,32 @@ def decode_layers(layers: list, page_table: torch.Tensor, seq_lens: torch.Tensor
         else:
             arr[i] = NvkvLayer(PREC_FP8, L["q"].data_ptr(), pool["k"].data_ptr(), None, pool["v"].data_ptr(), None,
                                L["k_gscale"], L["v_gscale"], L["out"].data_ptr())
-    _check("nvkv_decode_layers", _lib.nvkv_decode_layers(
-        ctypes.cast(arr, ctypes.c_void_p), len(layers), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), b, hq,
-        num_kv_heads, HEAD_DIM, PAGE_SIZE, sm_scale, pps, ns, _ptr(workspace), ws_bytes, _stream(q0)))
+    args = (ctypes.cast(arr, ctypes.c_void_p), len(layers), _ptr(page_table), page_table.shape[1], _ptr(seq_lens), b,
+            hq, num_kv_heads, HEAD_DIM, PAGE_SIZE, sm_scale, pps, ns, _ptr(workspace), ws_bytes, None)
+    keep = (arr, [dict(L) for L in layers], page_table, seq_lens, workspace)
+    return args, keep, q0
+
+
+def decode_layers(layers: list, page_table: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float, plan,
+                  num_kv_heads: int, workspace=None):
+    """One decode step across layers.  Each entry: dict(precision, q, pool, k_gscale, v_gscale, out)."""
+    args, keep, q0 = _decode_layers_args(layers, page_table, seq_lens, sm_scale, plan, num_kv_heads, workspace)
+    _check("nvkv_decode_layers", _lib.nvkv_decode_layers(*args[:-1], _stream(q0)))
     return [L["out"] for L in layers]
+
+
+def prepare_decode_layers(layers: list, page_table: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float, plan,
+                          num_kv_heads: int, workspace=None):
+    """decode_layers validated and marshalled once (the layer table is built once); ``run()`` re-issues it."""
+    args, keep, q0 = _decode_layers_args(layers, page_table, seq_lens, sm_scale, plan, num_kv_heads, workspace)
+    return PreparedCall(_lib.nvkv_decode_layers, args, keep, q0)
 
 
 # ------------------------------------------------------------------------------------------------
 # a6: prefix -> FP8 workspace
 # ------------------------------------------------------------------------------------------------
-def dequant_to_workspace(pool: dict, k_gscale: float, v_gscale: float, page_table: torch.Tensor,
-                         prefix_lens: torch.Tensor, ws_offsets: torch.Tensor, max_prefix_len: int,
-                         k_ws_scale: float, v_ws_scale: float, num_kv_heads: int, k_ws=None, v_ws=None):
+def _dequant_args(pool, k_gscale, v_gscale, page_table, prefix_lens, ws_offsets, max_prefix_len, k_ws_scale,
+                  v_ws_scale, num_kv_heads, k_ws, v_ws):
     _need(page_table, torch.int32, "page_table")
     _need(prefix_lens, torch.int32, "prefix_lens")
     _need(ws_offsets, torch.int32, "ws_offsets")
@@ -323,11 +349,27 @@ def dequant_to_workspace(pool: dict, k_gscale: float, v_gscale: float, page_tabl
         raise ValueError("k_ws and v_ws ([rows][H_kv][128] uint8) must be given")
     _need(k_ws, torch.uint8, "k_ws")
     _need(v_ws, torch.uint8, "v_ws")
-    _check("nvfp4_dequant_to_workspace", _lib.nvfp4_dequant_to_workspace(
-        _ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]), _ptr(pool["v_scale"]), k_gscale, v_gscale,
-        _ptr(page_table), page_table.shape[1], _ptr(prefix_lens), _ptr(ws_offsets), b, num_kv_heads, HEAD_DIM,
-        PAGE_SIZE, max_prefix_len, k_ws_scale, v_ws_scale, _ptr(k_ws), _ptr(v_ws), _stream(k_ws)))
+    return (_ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]), _ptr(pool["v_scale"]), k_gscale,
+            v_gscale, _ptr(page_table), page_table.shape[1], _ptr(prefix_lens), _ptr(ws_offsets), b, num_kv_heads,
+            HEAD_DIM, PAGE_SIZE, max_prefix_len, k_ws_scale, v_ws_scale, _ptr(k_ws), _ptr(v_ws), None)
+
+
+def dequant_to_workspace(pool: dict, k_gscale: float, v_gscale: float, page_table: torch.Tensor,
+                         prefix_lens: torch.Tensor, ws_offsets: torch.Tensor, max_prefix_len: int,
+                         k_ws_scale: float, v_ws_scale: float, num_kv_heads: int, k_ws=None, v_ws=None):
+    args = _dequant_args(pool, k_gscale, v_gscale, page_table, prefix_lens, ws_offsets, max_prefix_len, k_ws_scale,
+                         v_ws_scale, num_kv_heads, k_ws, v_ws)
+    _check("nvfp4_dequant_to_workspace", _lib.nvfp4_dequant_to_workspace(*args[:-1], _stream(k_ws)))
     return k_ws, v_ws
+
+
+def prepare_dequant_to_workspace(pool, k_gscale, v_gscale, page_table, prefix_lens, ws_offsets, max_prefix_len,
+                                 k_ws_scale, v_ws_scale, num_kv_heads, k_ws, v_ws):
+    """dequant_to_workspace validated and marshalled once; ``run()`` re-issues it (same buffers)."""
+    args = _dequant_args(pool, k_gscale, v_gscale, page_table, prefix_lens, ws_offsets, max_prefix_len, k_ws_scale,
+                         v_ws_scale, num_kv_heads, k_ws, v_ws)
+    return PreparedCall(_lib.nvfp4_dequant_to_workspace, args,
+                        (pool, page_table, prefix_lens, ws_offsets, k_ws, v_ws), k_ws)
 
 
 def default_sm_scale() -> float:

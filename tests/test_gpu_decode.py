@@ -171,6 +171,16 @@ def test_decode_layers_mixed_stack(nv):
     torch.cuda.synchronize()
     for i, (o, w) in enumerate(zip(outs, wants)):
         H.assert_attention_close(o.cpu().numpy(), w, f"layer {i}")
+    # the prepared form issues the same launches: bitwise equal results, call after call
+    first = [o.clone() for o in outs]
+    for L in layers:
+        L["out"] = torch.full_like(L["out"], float("nan"))
+    call = nv.prepare_decode_layers(layers, pt, sl, wl.sm_scale, plan, wl.h_kv)
+    for _ in range(2):
+        call.run()
+        torch.cuda.synchronize()
+        for i, L in enumerate(layers):
+            assert torch.equal(L["out"], first[i]), f"prepared layer {i}"
 
 
 def _sampled_full_size(nv, index, samples):

@@ -147,6 +147,13 @@ def test_nvfp4_quantize_fp8_input_bitexact(nv):
                              torch.from_numpy(slots).to(DEV), float(gk), float(gv), pool,
                              k_in_scale=float(sk), v_in_scale=float(sv))
     _check_pool(pool, want)
+    # the prepared form writes the same bytes
+    pool2 = nv.alloc_nvfp4_pool(4, h, DEV)
+    call = nv.prepare_nvfp4_quantize_append(torch.from_numpy(b).to(DEV), torch.from_numpy(b[::-1].copy()).to(DEV),
+                                            torch.from_numpy(slots).to(DEV), float(gk), float(gv), pool2,
+                                            k_in_scale=float(sk), v_in_scale=float(sv))
+    call.run()
+    _check_pool(pool2, want)
 
 
 def test_fp8_quantize_bitexact(nv):
@@ -191,3 +198,13 @@ def test_dequant_to_workspace_bitexact(nv):
                             float(s_wk), float(s_wv), wl.h_kv, kw, vw)
     assert np.array_equal(kw.cpu().numpy(), want_k)
     assert np.array_equal(vw.cpu().numpy(), want_v)
+    # the prepared form, issued twice into fresh buffers, writes the same bytes
+    kw2 = torch.full_like(kw, 0xEE)
+    vw2 = kw2.clone()
+    call = nv.prepare_dequant_to_workspace(pool, float(gk), float(gv), torch.from_numpy(wl.page_table).to(DEV),
+                                           torch.from_numpy(prefix).to(DEV), torch.from_numpy(offs).to(DEV),
+                                           int(prefix.max()), float(s_wk), float(s_wv), wl.h_kv, kw2, vw2)
+    for _ in range(2):
+        call.run()
+        assert np.array_equal(kw2.cpu().numpy(), want_k)
+        assert np.array_equal(vw2.cpu().numpy(), want_v)
