@@ -70,16 +70,57 @@ __device__ __forceinline__ uint32_t nvfp4_code(float x, float den) {
   return sgn | (den == 0.0f ? 0u : e2m1_encode_mag(fabsf(x / den)));
 }
 
-// Quantize 16 fp32 values of one block.  Returns the E4M3 scale byte; codes[i] gets the 4-bit
-// E2M1 code (sign in bit 3).  g is the tensor's global scale (> 0).
-__device__ __forceinline__ uint32_t nvfp4_quantize_block(const float (&x)[16], float g, uint32_t (&codes)[16]) {
+// Quantize 16 fp32 values of one block.  Returns the E4M3 scale byte; the 4-bit E2M1 codes (sign
+// in bit 3) come packed, element i in bits 4 (i % 8) of word i / 8 (lo: 0..7, hi: 8..15).  g is the
+// tensor's global scale (> 0).
+//
+// The codes are those of the correctly rounded quotients fp32(x / den), without dividing per value:
+//  * gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds an fp32 value to E2M1 exactly like the
+//    encoder above (nearest, ties to the even code, saturating, sign kept; checked on the device for
+//    every non-NaN fp32 bit pattern);
+//  * for den in [2^-100, 2^100], q0 = x * fp32(1 / den) is within 3 ulps of fp32(x / den) (two
+//    roundings of relative size <= 2^-24 each), so the two can round to different E2M1 codes only if
+//    an E2M1 rounding threshold (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5: fp32 values whose low 21
+//    significand bits are zero) lies within 3 ulps of q0.  A block with such a value, or with den
+//    outside that range, takes the correctly rounded division for all 16 values.  den == 0 (the
+//    block scale rounded to zero) gives signed zero codes through q = x * 0.
+__device__ __forceinline__ uint32_t nvfp4_quantize_block_packed(const float (&x)[16], float g, uint32_t& lo,
+                                                                uint32_t& hi) {
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
   float den;
   const uint32_t sc = nvfp4_block_scale(a, g, &den);
+  float q[16];
+  bool exact = den >= 0x1p-100f && den <= 0x1p100f;
+  if (exact) {
+    const float r = 1.0f / den;
+    bool near = false;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) codes[i] = nvfp4_code(x[i], den);
+    for (int i = 0; i < 16; ++i) {
+      q[i] = x[i] * r;
+      // bit distance to the nearest multiple of 2^21 (as a pattern), shifted so that the threshold
+      // range [0.25, 5] (patterns 0x3E800000 .. 0x40A00000) starts at 0
+      const uint32_t key = (__float_as_uint(q[i]) & 0x7FFFFFFFu) + (8u - 0x3E800000u);
+      near |= key <= 0x02200010u && (key & 0x1FFFFFu) <= 16u;
+    }
+    exact = !near;
+  }
+  if (!exact) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = den == 0.0f ? x[i] * 0.0f : x[i] / den;
+  }
+  uint32_t w0 = 0, w1 = 0;
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, q[0], q[1], 1.0f, 0);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, q[2], q[3], 1.0f, 1);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, q[4], q[5], 1.0f, 2);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, q[6], q[7], 1.0f, 3);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, q[8], q[9], 1.0f, 0);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, q[10], q[11], 1.0f, 1);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, q[12], q[13], 1.0f, 2);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, q[14], q[15], 1.0f, 3);
+  lo = w0;
+  hi = w1;
   return sc;
 }
 

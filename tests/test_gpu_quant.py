@@ -123,6 +123,39 @@ def test_nvfp4_quantize_golden_and_edge_blocks_bitexact(nv):
         assert flat[i].tolist() == blk["codes"], blk["name"]
 
 
+def test_nvfp4_quantize_near_rounding_thresholds_bitexact(nv):
+    """Values whose quotient x / (s g) falls within a few ulps of an E2M1 rounding threshold (0.25,
+    0.75, 1.25, 1.75, 2.5, 3.5, 5), on both sides and exactly on it, for several global scales: the
+    codes must still be those of the correctly rounded fp32 quotient."""
+    thresholds = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    xs = [1.0, 1.3984375, -0.6015625, 37.5]                     # bf16-exact
+    cases = 0
+    for t in thresholds:
+        for x0 in xs:
+            for k in list(range(-12, 13)) + [-40, -20, 20, 40]:
+                # g such that x0 / g is k ulps away from t (one E4M3 block scale of 1.0: amax ~ 5.9 g)
+                q = np.float32(t) * np.float32(1.0 + k * 2.0 ** -23)
+                g = np.float32(np.float32(abs(x0)) / q)
+                if not (np.isfinite(g) and g > 0):
+                    continue
+                a = _bf16(np.array([5.9 * float(g)])).float().numpy()[0]
+                blk = np.array([a, x0, -x0, x0] + [x0 * (1 - 2.0 ** -8 * i) for i in range(12)], dtype=np.float32)
+                tok = _bf16(np.tile(blk, 8)).float().numpy().reshape(1, 1, 128)
+                slots = np.array([3], dtype=np.int32)
+                dshape, sshape = o_layout.nvfp4_pool_shapes(1, 1)
+                want = {kk: np.zeros(sh, np.uint8) for kk, sh in (("k_data", dshape), ("k_scale", sshape),
+                                                                 ("v_data", dshape), ("v_scale", sshape))}
+                c, sc = o_nv.quantize_blocks(tok, g)
+                o_layout.write_nvfp4_tokens(want["k_data"], want["k_scale"], "k", slots, c, sc)
+                o_layout.write_nvfp4_tokens(want["v_data"], want["v_scale"], "v", slots, c, sc)
+                pool = nv.alloc_nvfp4_pool(1, 1, DEV)
+                tt = _bf16(tok).to(DEV)
+                nv.nvfp4_quantize_append(tt, tt.clone(), torch.from_numpy(slots).to(DEV), float(g), float(g), pool)
+                _check_pool(pool, want)
+                cases += 1
+    assert cases > 800
+
+
 def test_nvfp4_quantize_fp8_input_bitexact(nv):
     rng = np.random.default_rng(9)
     n_tok, h = 40, 2
@@ -174,13 +207,21 @@ def test_fp8_quantize_bitexact(nv):
     assert np.array_equal(pool["v"].cpu().numpy(), want_v)
 
 
-def test_dequant_to_workspace_bitexact(nv):
-    wl = workloads.Workload(name="ws-small", seed=13, batch=3, h_kv=2, h_q=4, seq_lens=[50, 16, 129])
+@pytest.mark.parametrize("case", ["small", "many-pages"])
+def test_dequant_to_workspace_bitexact(nv, case):
+    if case == "small":
+        wl = workloads.Workload(name="ws-small", seed=13, batch=3, h_kv=2, h_q=4, seq_lens=[50, 16, 129])
+        prefix = np.array([37, 16, 129], dtype=np.int32)
+    else:
+        # more (page, head) units than resident waves: each wave transcodes several pages in turn,
+        # with a ragged last round and a partial last page
+        wl = workloads.Workload(name="ws-many", seed=14, batch=2, h_kv=8, h_q=8, seq_lens=[13001, 9100])
+        prefix = np.array([13001, 9000], dtype=np.int32)
+    assert not wl.append
     ks, vs = H.oracle_inputs(wl)
-    gk, gv = H.oracle_nvfp4_scales(wl)
+    gk, gv = o_nv.global_scale(np.concatenate(ks)), o_nv.global_scale(np.concatenate(vs))
     s_wk, s_wv = np.float32(6.0) * gk, np.float32(6.0) * gv    # the layer's FP8 scale, amax / 448
-    prefix = np.array([37, 16, 129], dtype=np.int32)
-    offs = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int32) + np.array([0, 5, 5, 5], dtype=np.int32)
+    offs = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int32) + np.array([0] + [5] * wl.batch, dtype=np.int32)
     rows = int(offs[-1]) + 3
     want_k = np.full((rows, wl.h_kv, 128), 0xEE, np.uint8)
     want_v = want_k.copy()
