@@ -420,12 +420,13 @@ __global__ __launch_bounds__(64 * kWsWaves) void nvfp4_to_fp8_ws_kernel(
     const uint2 s0 = lut[1][w.vs_a & 0x7Fu], s1 = lut[1][w.vs_b & 0x7Fu];
     const uint2 va = ws_bytes8(s0, va0), vb = ws_bytes8(s0, va1), vc = ws_bytes8(s1, vb0), ve = ws_bytes8(s1, vb1);
     if (o < nv) {
-      // written once and read by a later kernel: streaming (non-temporal) stores
+      // plain stores: the two halves of each 128-byte row meet in L2 and leave it as whole lines
+      // (streaming stores of 64-byte halves raised the HBM write bytes by a third)
       const size_t row = (off + 16 * p + o) * row_bytes + (size_t)h * kHeadDim + 32 * grp;
-      __builtin_nontemporal_store(u4v{ka.x, ka.y, kb.x, kb.y}, reinterpret_cast<u4v*>(k_ws + row));
-      __builtin_nontemporal_store(u4v{kc.x, kc.y, ke.x, ke.y}, reinterpret_cast<u4v*>(k_ws + row + 16));
-      __builtin_nontemporal_store(u4v{va.x, va.y, vb.x, vb.y}, reinterpret_cast<u4v*>(v_ws + row));
-      __builtin_nontemporal_store(u4v{vc.x, vc.y, ve.x, ve.y}, reinterpret_cast<u4v*>(v_ws + row + 16));
+      *reinterpret_cast<uint4*>(k_ws + row) = make_uint4(ka.x, ka.y, kb.x, kb.y);
+      *reinterpret_cast<uint4*>(k_ws + row + 16) = make_uint4(kc.x, kc.y, ke.x, ke.y);
+      *reinterpret_cast<uint4*>(v_ws + row) = make_uint4(va.x, va.y, vb.x, vb.y);
+      *reinterpret_cast<uint4*>(v_ws + row + 16) = make_uint4(vc.x, vc.y, ve.x, ve.y);
     }
   };
   for (int u = u0; u < units; u += 2 * stride) {
