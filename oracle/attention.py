@@ -1,4 +1,4 @@
-"""fp64 decode attention on the dequantized cache (oracle, test infrastructure).
+"""fp64 decode and extend attention on the dequantized cache (oracle, test infrastructure).
 
 The decode path of the SGLang x Qwen x NVIDIA story ("Three Paths" paragraph 3)
 reads the NVFP4 cache, dequantizes on the fly and runs ordinary attention; the
@@ -46,3 +46,39 @@ def decode_attention(q, k_hat_seqs, v_hat_seqs, sm_scale) -> np.ndarray:
     q = np.asarray(q, dtype=np.float64)
     return np.stack([decode_attention_one(q[b], k_hat_seqs[b], v_hat_seqs[b], sm_scale)
                      for b in range(q.shape[0])])
+
+
+def extend_attention_one(q, k_hat, v_hat, prefix_len: int, sm_scale) -> np.ndarray:
+    """Chunked extend of one sequence: the chunk's queries attend over prefix || chunk, causally.
+
+    SGLang x Qwen x NVIDIA story, "Three Paths" paragraph 2 (extend gathers the cached prefix into
+    an FP8 workspace and attends over it together with the new chunk) and summary bullet 2 (the
+    prefill-side attention takes BF16 Q against FP8 KV).  The chunk's token i sits at position
+    prefix_len + i and sees keys 0 .. prefix_len + i (ordinary causal attention over the whole
+    sequence, restricted to the chunk's rows).
+
+    q [C][H_q][D]; k_hat, v_hat [prefix_len + C][H_kv][D] (fp64, the dequantized workspace rows)
+    -> out [C][H_q][D] fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_hat = np.asarray(k_hat, dtype=np.float64)
+    v_hat = np.asarray(v_hat, dtype=np.float64)
+    c, h_q, d = q.shape
+    total, h_kv, _ = k_hat.shape
+    if total != prefix_len + c or prefix_len < 0:
+        raise ValueError("k_hat / v_hat must hold prefix_len + C rows")
+    if h_q % h_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    group = h_q // h_kv
+    # key j is visible to chunk row i iff j <= prefix_len + i
+    visible = np.arange(total)[None, :] <= (prefix_len + np.arange(c))[:, None]      # [C][T]
+    out = np.empty((c, h_q, d), dtype=np.float64)
+    for hq in range(h_q):
+        hk = hq // group
+        z = float(sm_scale) * (q[:, hq, :] @ k_hat[:, hk, :].T)                       # [C][T]
+        z = np.where(visible, z, -np.inf)
+        z = z - z.max(axis=1, keepdims=True)
+        p = np.exp(z)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, hq, :] = p @ v_hat[:, hk, :]
+    return out
