@@ -30,6 +30,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 matrix-core peak of MI355X
 
 
 def parse():
@@ -194,6 +195,7 @@ def main():
     t_setup = time.perf_counter()
 
     # ---- build the step ------------------------------------------------------------------------
+    att_flops = 0            # extend: attention flops per launch
     if name in ("long", "batch32", "tiny", "ragged"):
         copies = 3 if name in ("batch32", "tiny") else 1
         pools = []
@@ -287,23 +289,47 @@ def main():
         k_ws = torch.empty((prefix + chunk, wl.h_kv, 128), dtype=torch.uint8, device=dev)   # shared by layers
         v_ws = torch.empty_like(k_ws)
 
-        calls = []
+        chunk_offs = torch.tensor([0, chunk], dtype=torch.int32, device=dev)
+        gen = torch.Generator().manual_seed(wl.seed * 7 + 5)
+        q_chunk = torch.randn((chunk, wl.h_q, 128), generator=gen).to(torch.bfloat16).to(dev)   # N(0,1) queries
+        att_out = torch.empty((chunk, wl.h_q, 128), dtype=torch.float32, device=dev)
+        layer_calls = []
         for pool, gk_l, gv_l, ck, cv in caches:
-            calls.append(nv.prepare_dequant_to_workspace(pool, gk_l, gv_l, pt, prefix_lens, offs, prefix, 6.0 * gk_l,
-                                                         6.0 * gv_l, wl.h_kv, k_ws, v_ws))
-            calls.append(nv.prepare_nvfp4_quantize_append(ck, cv, chunk_slots, gk_l, gv_l, pool))
+            s_wk, s_wv = 6.0 * gk_l, 6.0 * gv_l       # the layer's FP8 scale amax / 448
+            layer_calls.append((
+                nv.prepare_dequant_to_workspace(pool, gk_l, gv_l, pt, prefix_lens, offs, prefix, s_wk, s_wv, wl.h_kv,
+                                                k_ws, v_ws),
+                nv.prepare_fp8_workspace_append(ck, cv, chunk_offs, offs, prefix_lens, chunk, prefix, s_wk, s_wv,
+                                                wl.h_kv, k_ws, v_ws),
+                nv.prepare_fp8_extend_attn(q_chunk, chunk_offs, k_ws, v_ws, offs, prefix_lens, s_wk, s_wv,
+                                           wl.sm_scale, wl.h_kv, chunk, prefix, out=att_out)[0],
+                nv.prepare_nvfp4_quantize_append(ck, cv, chunk_slots, gk_l, gv_l, pool)))
+        att_events = []
 
         def step(events=None, i=0):
-            for call in calls:
-                call.run()
+            for gather, append, attend, quantize in layer_calls:
+                gather.run()
+                append.run()
+                if events is not None:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    attend.run()
+                    e1.record(stream)
+                    att_events.append((e0, e1))
+                else:
+                    attend.run()
+                quantize.run()
         # bytes: read prefix NVFP4 (144 B/token/head), write FP8 workspace (256 B), read chunk bf16 (512 B),
         # write chunk NVFP4 (144 B)
         step_bytes = len(caches) * wl.h_kv * (prefix * (144 + 256) + chunk * (512 + 144))
-        timed_kernel = None
+        # attention flops per launch: 4 * 128 per (query row, head, visible key)
+        att_flops = 4 * 128 * wl.h_q * (chunk * prefix + chunk * (chunk + 1) // 2)
+        timed_kernel = "extend_attn_kernel"
         kernel_bytes = None
-        desc = (f"extend: {len(caches)} NVFP4 layers x (16384-token prefix -> shared FP8 workspace + "
-                f"2048-token chunk quantize-append), 8 KV heads")
-        extra = {"layers": len(caches), "prefix": prefix, "chunk": chunk, "kv_heads": wl.h_kv}
+        desc = (f"extend: {len(caches)} NVFP4 layers x (16384-token prefix -> shared FP8 workspace, 2048-token chunk "
+                f"-> FP8 workspace, causal attention of the chunk's 32 query heads over prefix || chunk, chunk "
+                f"quantize-append), 8 KV heads")
+        extra = {"layers": len(caches), "prefix": prefix, "chunk": chunk, "kv_heads": wl.h_kv, "q_heads": wl.h_q}
         tokens_per_step = chunk
 
     # ---- warm up, then time exactly K steps -------------------------------------------------------
@@ -312,7 +338,11 @@ def main():
     torch.cuda.synchronize()
     # the split kernel's own dispatch records one event pair per step (no commands are added to
     # the stream); the step as a whole is bracketed by device synchronisations
-    events = HipEventPairs(args.steps) if timed_kernel else None
+    events = None
+    if timed_kernel and timed_kernel.startswith("decode_split_kernel"):
+        events = HipEventPairs(args.steps)
+    elif timed_kernel == "extend_attn_kernel":
+        events = True          # the step records torch events around each attention launch
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -326,7 +356,15 @@ def main():
     step_gpu_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    if timed_kernel:
+    bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+    if timed_kernel == "extend_attn_kernel":
+        kms = [e0.elapsed_time(e1) for e0, e1 in att_events]
+        kernel_ms = sum(kms) / len(kms)
+        achieved = att_flops / (kernel_ms * 1e-3) / 1e12
+        bound, peak, unit = "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        timing = (f"{timed_kernel}: mean of {len(kms)} launches (min {min(kms) * 1e3:.1f} us, max "
+                  f"{max(kms) * 1e3:.1f} us), torch events on the launch stream around each launch")
+    elif timed_kernel:
         kms = events.elapsed_ms()
         events.close()
         kernel_ms = sum(kms) / len(kms)
@@ -342,7 +380,7 @@ def main():
         assert torch.isfinite(out).all().item(), "non-finite decode output"
     log(f"{args.steps} steps: wall {ms_per_step:.4f} ms/step, events {step_gpu_ms:.4f} ms/step, "
         f"{value:.1f} GB/s ({value / HBM_PEAK_GBS:.1%} of 8 TB/s); {timed_kernel} {kernel_ms * 1e3:.1f} us "
-        f"-> {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")
+        f"-> {achieved:.1f} {unit} ({achieved / peak:.1%} of {peak:.0f})")
 
     cpu = None
     if not args.no_cpu_baseline and name in ("long", "batch32", "ragged", "tiny"):
@@ -378,9 +416,11 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens_per_step / (ms_per_step * 1e-3), 1),
         "kv_bytes_per_step": step_bytes,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": timed_kernel,
-                     "kernel_us": round(kernel_ms * 1e3, 2), "bytes_per_launch": kernel_bytes or step_bytes,
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": timed_kernel,
+                     "kernel_us": round(kernel_ms * 1e3, 2),
+                     ("flops_per_launch" if bound == "mfma" else "bytes_per_launch"):
+                         att_flops if bound == "mfma" else (kernel_bytes or step_bytes),
                      "traffic_detail": traffic_detail, "timing": timing},
         "cpu_baseline": cpu,
     }

@@ -54,6 +54,8 @@ EXPORTED = {
     "nvkv_decode_layers": (_i, [_p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p, _sz, _p]),
     "nvfp4_dequant_to_workspace": (_i, [_p, _p, _p, _p, _f, _f, _p, _i, _p, _p, _i, _i, _i, _i, _i, _f, _f, _p, _p,
                                         _p]),
+    "fp8_workspace_append": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _f, _p, _p, _p]),
+    "fp8_extend_attn": (_i, [_p, _p, _p, _p, _p, _p, _f, _f, _f, _i, _i, _i, _i, _i, _i, _p, _p]),
 }
 for _name, (_res, _args) in EXPORTED.items():
     _fn = getattr(_lib, _name)
@@ -370,6 +372,82 @@ def prepare_dequant_to_workspace(pool, k_gscale, v_gscale, page_table, prefix_le
                          v_ws_scale, num_kv_heads, k_ws, v_ws)
     return PreparedCall(_lib.nvfp4_dequant_to_workspace, args,
                         (pool, page_table, prefix_lens, ws_offsets, k_ws, v_ws), k_ws)
+
+
+# ------------------------------------------------------------------------------------------------
+# NEXT 1: the extend attention over the FP8 workspace
+# ------------------------------------------------------------------------------------------------
+def _extend_ints(chunk_offsets, ws_offsets, prefix_lens):
+    _need(chunk_offsets, torch.int32, "chunk_offsets")
+    _need(ws_offsets, torch.int32, "ws_offsets")
+    _need(prefix_lens, torch.int32, "prefix_lens")
+    b = prefix_lens.numel()
+    if chunk_offsets.numel() != b + 1 or ws_offsets.numel() < b:
+        raise ValueError("chunk_offsets needs batch + 1 entries and ws_offsets at least batch")
+    return b
+
+
+def _ws_append_args(k, v, chunk_offsets, ws_offsets, prefix_lens, max_chunk_len, max_prefix_len, k_ws_scale,
+                    v_ws_scale, num_kv_heads, k_ws, v_ws):
+    _need(k, torch.bfloat16, "k")
+    _need(v, torch.bfloat16, "v")
+    if k.dim() != 3 or k.shape != v.shape or k.shape[1] != num_kv_heads or k.shape[2] != HEAD_DIM:
+        raise ValueError("k, v must be [total_chunk][H_kv][128]")
+    _need(k_ws, torch.uint8, "k_ws")
+    _need(v_ws, torch.uint8, "v_ws")
+    b = _extend_ints(chunk_offsets, ws_offsets, prefix_lens)
+    return (_ptr(k), _ptr(v), _ptr(chunk_offsets), _ptr(ws_offsets), _ptr(prefix_lens), b, num_kv_heads, HEAD_DIM,
+            max_chunk_len, max_prefix_len, k_ws_scale, v_ws_scale, _ptr(k_ws), _ptr(v_ws), None)
+
+
+def fp8_workspace_append(k, v, chunk_offsets, ws_offsets, prefix_lens, max_chunk_len, max_prefix_len, k_ws_scale,
+                         v_ws_scale, num_kv_heads, k_ws, v_ws):
+    """The chunk's bf16 K/V -> FP8 workspace rows after each sequence's prefix."""
+    args = _ws_append_args(k, v, chunk_offsets, ws_offsets, prefix_lens, max_chunk_len, max_prefix_len, k_ws_scale,
+                           v_ws_scale, num_kv_heads, k_ws, v_ws)
+    _check("fp8_workspace_append", _lib.fp8_workspace_append(*args[:-1], _stream(k)))
+
+
+def prepare_fp8_workspace_append(k, v, chunk_offsets, ws_offsets, prefix_lens, max_chunk_len, max_prefix_len,
+                                 k_ws_scale, v_ws_scale, num_kv_heads, k_ws, v_ws):
+    args = _ws_append_args(k, v, chunk_offsets, ws_offsets, prefix_lens, max_chunk_len, max_prefix_len, k_ws_scale,
+                           v_ws_scale, num_kv_heads, k_ws, v_ws)
+    return PreparedCall(_lib.fp8_workspace_append, args, (k, v, chunk_offsets, ws_offsets, prefix_lens, k_ws, v_ws), k)
+
+
+def _extend_args(q, chunk_offsets, k_ws, v_ws, ws_offsets, prefix_lens, k_ws_scale, v_ws_scale, sm_scale,
+                 num_kv_heads, max_chunk_len, max_prefix_len, out):
+    _need(q, torch.bfloat16, "q")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [total_chunk][H_q][128]")
+    _need(k_ws, torch.uint8, "k_ws")
+    _need(v_ws, torch.uint8, "v_ws")
+    b = _extend_ints(chunk_offsets, ws_offsets, prefix_lens)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    args = (_ptr(q), _ptr(chunk_offsets), _ptr(k_ws), _ptr(v_ws), _ptr(ws_offsets), _ptr(prefix_lens), k_ws_scale,
+            v_ws_scale, sm_scale, b, q.shape[1], num_kv_heads, HEAD_DIM, max_chunk_len, max_prefix_len, _ptr(out),
+            None)
+    return args, out
+
+
+def fp8_extend_attn(q, chunk_offsets, k_ws, v_ws, ws_offsets, prefix_lens, k_ws_scale, v_ws_scale, sm_scale,
+                    num_kv_heads, max_chunk_len, max_prefix_len, out=None):
+    """Chunk queries (bf16) attend causally over prefix || chunk in the FP8 workspace -> fp32 out."""
+    args, out = _extend_args(q, chunk_offsets, k_ws, v_ws, ws_offsets, prefix_lens, k_ws_scale, v_ws_scale, sm_scale,
+                             num_kv_heads, max_chunk_len, max_prefix_len, out)
+    _check("fp8_extend_attn", _lib.fp8_extend_attn(*args[:-1], _stream(q)))
+    return out
+
+
+def prepare_fp8_extend_attn(q, chunk_offsets, k_ws, v_ws, ws_offsets, prefix_lens, k_ws_scale, v_ws_scale, sm_scale,
+                            num_kv_heads, max_chunk_len, max_prefix_len, out=None):
+    args, out = _extend_args(q, chunk_offsets, k_ws, v_ws, ws_offsets, prefix_lens, k_ws_scale, v_ws_scale, sm_scale,
+                             num_kv_heads, max_chunk_len, max_prefix_len, out)
+    return PreparedCall(_lib.fp8_extend_attn, args, (q, chunk_offsets, k_ws, v_ws, ws_offsets, prefix_lens, out), q), out
 
 
 def default_sm_scale() -> float:

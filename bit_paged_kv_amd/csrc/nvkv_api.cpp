@@ -342,4 +342,50 @@ int nvfp4_dequant_to_workspace(const uint8_t* k_data, const uint8_t* k_scale, co
                                                   stream));
 }
 
+static int extend_common_status(int batch, int num_kv_heads, int head_dim, int max_chunk_len, int max_prefix_len,
+                                float k_ws_scale, float v_ws_scale) {
+  if (head_dim <= 0) return NVKV_E_INVAL;
+  if (head_dim != kD) return NVKV_E_UNSUPPORTED;
+  if (batch < 1 || batch > 65535 || num_kv_heads < 1 || num_kv_heads > 65535) return NVKV_E_INVAL;
+  if (max_chunk_len < 0 || max_prefix_len < 0) return NVKV_E_INVAL;
+  if (!good_scale(k_ws_scale) || !good_scale(v_ws_scale)) return NVKV_E_INVAL;
+  // workspace rows of one sequence are addressed with 32-bit byte offsets
+  if (((long long)max_prefix_len + max_chunk_len) * num_kv_heads * kD >= (1LL << 31)) return NVKV_E_INVAL;
+  return NVKV_OK;
+}
+
+int fp8_workspace_append(const void* k, const void* v, const int32_t* chunk_offsets, const int32_t* ws_offsets,
+                         const int32_t* prefix_lens, int batch, int num_kv_heads, int head_dim, int max_chunk_len,
+                         int max_prefix_len, float k_ws_scale, float v_ws_scale, uint8_t* k_ws, uint8_t* v_ws,
+                         hipStream_t stream) {
+  int st = extend_common_status(batch, num_kv_heads, head_dim, max_chunk_len, max_prefix_len, k_ws_scale, v_ws_scale);
+  if (st) return st;
+  if (!k || !v || !chunk_offsets || !ws_offsets || !prefix_lens || !k_ws || !v_ws) return NVKV_E_INVAL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_ws, 16) || !aligned(v_ws, 16) || !aligned(chunk_offsets, 4) ||
+      !aligned(ws_offsets, 4) || !aligned(prefix_lens, 4))
+    return NVKV_E_INVAL;
+  if (max_chunk_len == 0) return NVKV_OK;
+  return launch_status(nvkv::launch_fp8_ws_append(k, v, chunk_offsets, ws_offsets, prefix_lens, batch, num_kv_heads,
+                                                  max_chunk_len, k_ws_scale, v_ws_scale, k_ws, v_ws, stream));
+}
+
+int fp8_extend_attn(const void* q, const int32_t* chunk_offsets, const uint8_t* k_ws, const uint8_t* v_ws,
+                    const int32_t* ws_offsets, const int32_t* prefix_lens, float k_ws_scale, float v_ws_scale,
+                    float sm_scale, int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_chunk_len,
+                    int max_prefix_len, float* out, hipStream_t stream) {
+  int st = extend_common_status(batch, num_kv_heads, head_dim, max_chunk_len, max_prefix_len, k_ws_scale, v_ws_scale);
+  if (st) return st;
+  st = heads_status(num_q_heads, num_kv_heads);
+  if (st) return st;
+  if (!(isfinite(sm_scale) && sm_scale > 0.0f)) return NVKV_E_INVAL;
+  if (!q || !chunk_offsets || !k_ws || !v_ws || !ws_offsets || !prefix_lens || !out) return NVKV_E_INVAL;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_ws, 16) || !aligned(v_ws, 16) || !aligned(chunk_offsets, 4) ||
+      !aligned(ws_offsets, 4) || !aligned(prefix_lens, 4))
+    return NVKV_E_INVAL;
+  if (max_chunk_len == 0) return NVKV_OK;
+  return launch_status(nvkv::launch_extend_attn(q, chunk_offsets, k_ws, v_ws, ws_offsets, prefix_lens, k_ws_scale,
+                                                v_ws_scale, sm_scale, batch, num_q_heads, num_kv_heads,
+                                                max_chunk_len, out, stream));
+}
+
 }  // extern "C"

@@ -23,6 +23,14 @@ hipError_t launch_dequant_to_ws(const uint8_t* k_data, const uint8_t* k_scale, c
                                 int max_prefix, float sk_ws, float sv_ws, uint8_t* k_ws, uint8_t* v_ws,
                                 hipStream_t stream);
 
+hipError_t launch_fp8_ws_append(const void* k, const void* v, const int32_t* chunk_offsets, const int32_t* ws_offsets,
+                                const int32_t* prefix_lens, int batch, int hkv, int max_chunk, float sk, float sv,
+                                uint8_t* k_ws, uint8_t* v_ws, hipStream_t stream);
+hipError_t launch_extend_attn(const void* q, const int32_t* chunk_offsets, const uint8_t* k_ws, const uint8_t* v_ws,
+                              const int32_t* ws_offsets, const int32_t* prefix_lens, float k_ws_scale,
+                              float v_ws_scale, float sm_scale, int batch, int hq, int hkv, int max_chunk,
+                              float* out, hipStream_t stream);
+
 // Decode: one workgroup of four wavefronts per (sequence, kv head, split); with several splits a
 // second kernel merges the partial softmax states.
 enum CacheFormat { kFmtNvfp4 = 0, kFmtFp8 = 1 };

@@ -243,6 +243,50 @@ NVKV_API int nvfp4_dequant_to_workspace(const uint8_t* k_data, const uint8_t* k_
                                float k_ws_scale, float v_ws_scale,
                                uint8_t* k_ws, uint8_t* v_ws, hipStream_t stream);
 
+/*
+ * fp8_workspace_append -- the extend chunk's own K/V join its prefix in the FP8 workspace ([S]
+ * "Three Paths" paragraph 2: the extend attention runs over prefix || chunk in FP8):
+ *     w = E4M3_rne_sat(fp32(x / ws_scale)), x the bf16 value (the FP8 encoding of the mixed-precision
+ *     layers, [O] "03 Mixed-precision KV Cache").
+ *   k, v          : [total_chunk][num_kv_heads][128] bf16, device: the chunks of all sequences,
+ *                   concatenated; sequence b's rows are chunk_offsets[b] .. chunk_offsets[b+1]-1.
+ *   chunk_offsets : [batch + 1] int32, device, non-decreasing; chunk lengths <= max_chunk_len.
+ *   ws_offsets, prefix_lens : as for nvfp4_dequant_to_workspace; chunk row i of sequence b goes to
+ *                   workspace row ws_offsets[b] + prefix_lens[b] + i.
+ *   max_chunk_len, max_prefix_len : host upper bounds (grid size, offset range checks).
+ * Bytes are written only to those rows.  Errors: NVKV_E_INVAL for null / misaligned pointers (16
+ * bytes for k, v, k_ws, v_ws; 4 for the int32 arrays), batch outside [1, 65535], negative bounds,
+ * bad scales, or a workspace span (max_prefix_len + max_chunk_len) * num_kv_heads * 128 of 2^31
+ * bytes or more; NVKV_E_UNSUPPORTED for head_dim != 128.  max_chunk_len == 0 is a no-op.
+ */
+NVKV_API int fp8_workspace_append(const void* k, const void* v, const int32_t* chunk_offsets,
+                         const int32_t* ws_offsets, const int32_t* prefix_lens,
+                         int batch, int num_kv_heads, int head_dim, int max_chunk_len, int max_prefix_len,
+                         float k_ws_scale, float v_ws_scale, uint8_t* k_ws, uint8_t* v_ws, hipStream_t stream);
+
+/*
+ * fp8_extend_attn -- chunked-extend attention ([S] "Three Paths" paragraph 2; summary bullet 2:
+ * BF16 Q against FP8 KV): the chunk's queries attend over their sequence's prefix || chunk in the
+ * FP8 workspace, causally.  For chunk row i of sequence b and query head hq (kv head hq / G):
+ *     z_j = sm_scale * <q, k_ws_scale * e4m3(K_j)>,  j = 0 .. prefix_lens[b] + i,
+ *     out = v_ws_scale * sum_j softmax(z)_j e4m3(V_j),
+ * with key j at workspace row ws_offsets[b] + j (the prefix rows, then the chunk rows).
+ *   q             : [total_chunk][num_q_heads][128] bf16, device, rows as chunk_offsets.
+ *   k_ws, v_ws    : [rows][num_kv_heads][128] E4M3, device (written by nvfp4_dequant_to_workspace
+ *                   and fp8_workspace_append).
+ *   out           : [total_chunk][num_q_heads][128] fp32, device; every row of every chunk is written.
+ *   max_chunk_len, max_prefix_len : host upper bounds of the chunk lengths and prefix_lens.
+ * Computed with bf16 q x bf16 K (exact from E4M3) on the matrix cores, fp32 scores, fp16 softmax
+ * weights x fp16 V (exact from E4M3), fp32 accumulation.  Errors as fp8_workspace_append, plus
+ * NVKV_E_INVAL / NVKV_E_UNSUPPORTED for the head counts (as the decode calls) and a bad sm_scale.
+ */
+NVKV_API int fp8_extend_attn(const void* q, const int32_t* chunk_offsets,
+                    const uint8_t* k_ws, const uint8_t* v_ws,
+                    const int32_t* ws_offsets, const int32_t* prefix_lens,
+                    float k_ws_scale, float v_ws_scale, float sm_scale,
+                    int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                    int max_chunk_len, int max_prefix_len, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

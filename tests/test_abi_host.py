@@ -30,7 +30,7 @@ def _declared():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib._lib, n), f"{n} not exported by libnvkv.so"
         assert n in lib.EXPORTED, f"{n} has no binding"
@@ -185,3 +185,28 @@ def test_global_scale_and_dequant_validation(lib):
     assert d(*bad) == UNSUP
     ok0 = list(args); ok0[14] = 0                                 # nothing to gather: no launch
     assert d(*ok0) == OK
+
+
+def test_extend_validation(lib):
+    """The extend calls reject bad arguments; a zero chunk bound is a no-op (no launch)."""
+    ap = lib._lib.fp8_workspace_append
+    #       k  v  chunk_off ws_off prefix batch hkv D    max_c max_p  sk   sv   k_ws v_ws stream
+    base = [A, A, A,        A,     A,     2,    8,  128, 64,   1024,  1.0, 1.0, A,   A,   S]
+    assert ap(*base[:8], 0, *base[9:]) == OK
+    mis4 = A + 2                                      # not 4-byte aligned (int32 arrays)
+    for i, v, want in ((0, None, INVAL), (1, MIS, INVAL), (2, mis4, INVAL), (4, None, INVAL), (5, 0, INVAL),
+                       (5, 70000, INVAL), (6, 0, INVAL), (7, 64, UNSUP), (8, -1, INVAL), (9, -1, INVAL),
+                       (10, 0.0, INVAL), (11, float("inf"), INVAL), (12, None, INVAL), (13, MIS, INVAL),
+                       (9, 1 << 21, INVAL)):                  # (prefix + chunk) * H_kv * 128 >= 2^31 bytes
+        a = list(base); a[i] = v
+        assert ap(*a) == want, (i, v)
+    ex = lib._lib.fp8_extend_attn
+    #       q  c_off k_ws v_ws ws_off prefix sk   sv   sm    batch hq  hkv D    max_c max_p out stream
+    base = [A, A,    A,   A,   A,     A,     1.0, 1.0, 0.09, 2,    32, 8,  128, 64,   1024, A,  S]
+    assert ex(*base[:13], 0, *base[14:]) == OK
+    for i, v, want in ((0, None, INVAL), (0, MIS, INVAL), (15, None, INVAL), (15, MIS, INVAL), (8, 0.0, INVAL),
+                       (8, float("nan"), INVAL), (10, 30, INVAL), (10, 8 * 17, UNSUP), (12, 96, UNSUP),
+                       (9, 0, INVAL), (13, -5, INVAL), (6, -1.0, INVAL), (14, 1 << 21, INVAL), (1, A + 2, INVAL),
+                       (4, None, INVAL)):
+        a = list(base); a[i] = v
+        assert ex(*a) == want, (i, v)
