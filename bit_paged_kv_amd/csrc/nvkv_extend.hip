@@ -10,7 +10,9 @@
 //    columns are (query token, query head of the group) pairs, 32 per wave, so every K/V tile
 //    staged in LDS serves all G query heads of the kv head;
 //  * K/V tiles of 32 keys are read from HBM once per workgroup, converted from E4M3 (exactly) to
-//    bf16 (K) and fp16 (V) while being written to LDS, double-buffered with one barrier per tile;
+//    bf16 (K) and fp16 (V) while being written to LDS, in three buffers with one barrier per tile:
+//    the PV products of a tile are issued after the next tile's QK products, so each wave has
+//    independent matrix work in flight while its softmax runs;
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (keys as rows, bf16 q as the B operand straight from
 //    registers): each lane ends with 4 keys x 1 column of scores -- exactly the B operand layout of
 //    O^T += V^T P^T on v_mfma_f32_16x16x32_f16, so softmax needs no data movement between the two;
@@ -73,7 +75,10 @@ constexpr int kXWaves = 4;
 constexpr int kXCols = 32 * kXWaves;     // score columns per workgroup
 constexpr int kXKeys = 32;               // keys per tile
 constexpr int kKRow = 128 + 8;           // bf16 elements per K row in LDS (16-byte pad: conflict-free reads)
-constexpr int kVQuad = 128 * 4 + 8;      // fp16 elements per V key quad in LDS ([channel][4 keys] + pad)
+// V in LDS: [g][channel][8 keys] fp16 with keys 4 g .. 4 g + 3 then 16 + 4 g .. 16 + 4 g + 3 of the tile,
+// i.e. exactly the 16-byte A operand (V^T row, k = 8 g .. 8 g + 7) lane group g reads for a channel
+// (+ 8 elements of pad per group: the staging writes of one pass then fall in 32 distinct bank pairs)
+constexpr int kVGroup = 128 * 8 + 8;     // fp16 elements per lane group
 constexpr float kXSlack = 8.0f;          // weights may reach 2^8 before the running maximum is raised
 
 typedef unsigned int u4x __attribute__((ext_vector_type(4)));
@@ -123,14 +128,15 @@ struct ExtendArgs {
   const int32_t* ws_offsets;    // [batch (+1)]
   const int32_t* prefix_lens;   // [batch]
   float qk_scale;               // sm_scale * s_K * log2(e)
+  float inv_qk_scale;           // 1 / qk_scale (raw-score threshold of the lazy rescale)
   float v_scale;                // s_V
   int hq, hkv, group, tokens_per_wg;
   float* out;                   // fp32 [total_q][hq][128]
 };
 
 __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kXKeys * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][(kXKeys / 4) * kVQuad];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[3][kXKeys * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[3][4 * kVGroup];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.z, hk = blockIdx.y;
@@ -173,10 +179,10 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
   }
 
   // ---- staging: thread t loads 16 K bytes (key t / 8, channels 16 (t % 8) ..) and 4 x 4 V bytes
-  //      (keys 4 (t / 32) .. + 3, channels 4 (t % 32) .. + 3) of a tile ----
+  //      (keys 4 (t % 8) .. + 3, channels 4 (t / 8) .. + 3) of a tile ----
   const int t = threadIdx.x;
   const int sk_key = t >> 3, sk_ch = (t & 7) * 16;
-  const int sv_q = t >> 5, sv_ch = (t & 31) * 4;
+  const int sv_q = t & 7, sv_ch = (t >> 3) * 4;
   uint4 kreg;
   uint32_t vreg[4];
   auto load_tile = [&](int tile) {
@@ -206,27 +212,52 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
       h[r][0] = fp8x2_to_f16x2<false>(vreg[r]);
       h[r][1] = fp8x2_to_f16x2<true>(vreg[r]);
     }
-    uint16_t* vd = &v_lds[buf][sv_q * kVQuad + sv_ch * 4];
+    // key quad sv_q is half sv_q / 4 of lane group sv_q % 4's 8-key rows
+    uint16_t* vd = &v_lds[buf][(sv_q & 3) * kVGroup + sv_ch * 8 + (sv_q >> 2) * 4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int wi = c >> 1;
       const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;   // high or low fp16 of each pair
       const uint32_t k01 = __builtin_amdgcn_perm(h[1][wi], h[0][wi], sel);
       const uint32_t k23 = __builtin_amdgcn_perm(h[3][wi], h[2][wi], sel);
-      *reinterpret_cast<uint2*>(vd + c * 4) = make_uint2(k01, k23);
+      *reinterpret_cast<uint2*>(vd + c * 8) = make_uint2(k01, k23);
     }
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f}, thr[2] = {-INFINITY, -INFINITY};
+  // a finite floor for the running maximum: exp2(score - m_run) needs no guard for columns that
+  // have seen no visible key yet (their weights are exp2(-inf) = 0, and the first real maximum
+  // rescales the empty state by exp2(-1e30 - m) = 0)
+  constexpr float kFloor = -1.0e30f;
+  float m_run[2] = {kFloor, kFloor}, l_run[2] = {0.0f, 0.0f}, thr[2] = {-INFINITY, -INFINITY};
   f4 o[8][2];
 #pragma unroll
   for (int n = 0; n < 8; ++n) o[n][0] = o[n][1] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // Software pipeline over three LDS buffers: iteration i computes S(i) = K(i) Q^T, then the PV
+  // products of tile i - 1 (independent of S(i), so the matrix cores stay busy while S(i) drains),
+  // then the softmax of tile i; tile i + 1 is staged meanwhile.  Buffers in use in iteration i:
+  // i % 3 (QK), (i - 1) % 3 (PV) and (i + 1) % 3 (staging) -- all distinct.
+  h8 phi[2], plo[2];   // B operands of PV for the previous tile: P^T hi / lo, keys 4 g + r then 16 + 4 g + r
+  auto pv = [&](int vb) {
+    // O^T += V^T P^T: A = V^T[16 n + lane % 16][keys 4 g + r, 16 + 4 g + r], one 16-byte read
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int ch = 16 * n + col16;
+      const h8 vop = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(&v_lds[vb][g * kVGroup + ch * 8]));
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, phi[ct], o[n][ct], 0, 0, 0);
+        o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, plo[ct], o[n][ct], 0, 0, 0);
+      }
+    }
+  };
+
   load_tile(0);
   store_tile(0);
   __syncthreads();
+  int buf = 0, prev = 2;
   for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
+    const int next = (buf == 2) ? 0 : buf + 1;
     if (tile + 1 < n_tiles) load_tile(tile + 1);
     const int key0 = tile * kXKeys;
     // S^T = K Q^T: rows are keys 16 rt + (lane % 16) of the tile
@@ -242,9 +273,9 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
         s[rt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[1][ks], s[rt][1], 0, 0, 0);
       }
     }
-    // this lane's keys: key0 + 16 rt + 4 g + r
+    if (tile > 0) pv(prev);
+    // softmax of this tile; this lane's keys: key0 + 16 rt + 4 g + r
     const bool edge = key0 + kXKeys > prefix + qt0;   // some column may not see every key of the tile
-    h8 phi[2], plo[2];   // B operands of PV: P^T hi and lo parts, keys 4 g + r then 16 + 4 g + r
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       float x[8];
@@ -265,17 +296,17 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
       if (__any(xm > thr[ct])) {
         const float hmax = xmax32(xmax16(xm));
         const float m_new = fmaxf(m_run[ct], hmax * a.qk_scale);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[ct] - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_new);
         l_run[ct] *= alpha;
 #pragma unroll
         for (int n = 0; n < 8; ++n) o[n][ct] *= alpha;
         m_run[ct] = m_new;
-        thr[ct] = (m_new == -INFINITY) ? -INFINITY : (m_new + kXSlack) / a.qk_scale;
+        thr[ct] = (m_new + kXSlack) * a.inv_qk_scale;
       }
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        p[i] = (m_run[ct] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], a.qk_scale, -m_run[ct]));
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], a.qk_scale, -m_run[ct]));
       l_run[ct] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       // P = hi + lo in fp16: hi rounds toward zero, lo = fp16(P - hi) keeps ~11 more bits
       h2 hp[4], lp[4];
@@ -287,22 +318,12 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
       phi[ct] = cat4(hp[0], hp[1], hp[2], hp[3]);
       plo[ct] = cat4(lp[0], lp[1], lp[2], lp[3]);
     }
-    // O^T += V^T P^T: A = V^T[16 n + lane % 16][keys 4 g + r, 16 + 4 g + r] from the quad layout
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int ch = 16 * n + col16;
-      const uint2 va = *reinterpret_cast<const uint2*>(&v_lds[buf][g * kVQuad + ch * 4]);
-      const uint2 vb = *reinterpret_cast<const uint2*>(&v_lds[buf][(4 + g) * kVQuad + ch * 4]);
-      const h8 vop = __builtin_bit_cast(h8, make_uint4(va.x, va.y, vb.x, vb.y));
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, phi[ct], o[n][ct], 0, 0, 0);
-        o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, plo[ct], o[n][ct], 0, 0, 0);
-      }
-    }
-    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+    if (tile + 1 < n_tiles) store_tile(next);
     __syncthreads();
+    prev = buf;
+    buf = next;
   }
+  pv(prev);   // the last tile's products (no buffer is written any more)
 
   // ---- normalise and write: lane holds O^T[16 n + 4 g + r][column] ----
 #pragma unroll
@@ -338,6 +359,7 @@ hipError_t launch_extend_attn(const void* q, const int32_t* q_offsets, const uin
   a.ws_offsets = ws_offsets;
   a.prefix_lens = prefix_lens;
   a.qk_scale = sm_scale * k_ws_scale * 1.44269504088896341f;
+  a.inv_qk_scale = 1.0f / a.qk_scale;
   a.v_scale = v_ws_scale;
   a.hq = hq;
   a.hkv = hkv;
