@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="long", choices=["long", "batch32", "ragged", "mixed", "extend", "tiny"])
+    ap.add_argument("--config", default="long", choices=["long", "batch32", "ragged", "mixed", "extend", "prefill",
+                                                         "tiny"])
     ap.add_argument("--pages-per-split", type=int, default=0, help="force the split size (0 = planner)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -189,7 +190,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     name = args.config
-    index = {"tiny": 0, "batch32": 1, "long": 2, "ragged": 3, "mixed": 4, "extend": 4}[name]
+    index = {"tiny": 0, "batch32": 1, "long": 2, "ragged": 3, "mixed": 4, "extend": 4, "prefill": 4}[name]
     wl = workloads.config(index)
     stream = torch.cuda.current_stream(dev)
     t_setup = time.perf_counter()
@@ -264,6 +265,56 @@ def main():
                  "fp8_layers": list(wl.fp8_layers), "kv_heads": wl.h_kv, "q_heads": wl.h_q,
                  "pages_per_split": plan[0], "num_splits": plan[1]}
         tokens_per_step = wl.batch
+    elif name == "prefill":
+        # per NVFP4 layer of the stack: a 16384-token prompt written once into the NVFP4 cache and the
+        # dense FP8 copy (one pass), then causal BF16-Q x FP8-KV attention over the copy
+        ext = workloads.Workload(name="prefill", seed=wl.seed, batch=1, h_kv=wl.h_kv, h_q=wl.h_q,
+                                 seq_lens=[wl.extend_prefix], chan=wl.chan)
+        nlayers = [l for l in range(wl.layers) if not wl.is_fp8(l)]
+        n_tok = wl.extend_prefix
+        slots = torch.from_numpy(ext.slots(0, 0, n_tok)).to(dev)
+        offs = torch.tensor([0, n_tok], dtype=torch.int32, device=dev)
+        zero = torch.zeros(1, dtype=torch.int32, device=dev)
+        gen = torch.Generator().manual_seed(wl.seed * 7 + 6)
+        q_all = torch.randn((n_tok, wl.h_q, 128), generator=gen).to(torch.bfloat16).to(dev)
+        att_out = torch.empty((n_tok, wl.h_q, 128), dtype=torch.float32, device=dev)
+        k_ws = torch.empty((n_tok, wl.h_kv, 128), dtype=torch.uint8, device=dev)    # shared by layers
+        v_ws = torch.empty_like(k_ws)
+        layer_calls = []
+        for layer in nlayers:
+            k = ext.kv("k", 0, layer).to(dev)
+            v = ext.kv("v", 0, layer).to(dev)
+            gk_l = float(nv.global_scale(k).item())
+            gv_l = float(nv.global_scale(v).item())
+            pool = nv.alloc_nvfp4_pool(ext.num_pages, wl.h_kv, dev)
+            s_wk, s_wv = 6.0 * gk_l, 6.0 * gv_l
+            layer_calls.append((
+                nv.prepare_nvfp4_prefill_write(k, v, slots, gk_l, gv_l, pool, s_wk, s_wv, k_ws, v_ws),
+                nv.prepare_fp8_extend_attn(q_all, offs, k_ws, v_ws, offs, zero, s_wk, s_wv, wl.sm_scale, wl.h_kv,
+                                           n_tok, 0, out=att_out)[0]))
+            log(f"layer {layer} prompt ready, {time.perf_counter() - t_setup:.1f} s")
+        att_events = []
+
+        def step(events=None, i=0):
+            for write, attend in layer_calls:
+                write.run()
+                if events is not None:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    attend.run()
+                    e1.record(stream)
+                    att_events.append((e0, e1))
+                else:
+                    attend.run()
+        # bytes of the write: read bf16 K+V (512 B per token-head), write NVFP4 (144 B) and FP8 (256 B)
+        step_bytes = len(layer_calls) * wl.h_kv * n_tok * (512 + 144 + 256)
+        att_flops = 4 * 128 * wl.h_q * (n_tok * (n_tok + 1) // 2)
+        timed_kernel = "extend_attn_kernel"
+        kernel_bytes = None
+        desc = (f"prefill: {len(layer_calls)} NVFP4 layers x (16384-token prompt -> NVFP4 cache + FP8 copy in one pass, "
+                f"causal attention of 32 query heads over the FP8 copy), 8 KV heads")
+        extra = {"layers": len(layer_calls), "prompt": n_tok, "kv_heads": wl.h_kv, "q_heads": wl.h_q}
+        tokens_per_step = n_tok
     else:  # extend
         ext = workloads.Workload(name="extend", seed=wl.seed, batch=1, h_kv=wl.h_kv, h_q=wl.h_q,
                                  seq_lens=[wl.extend_prefix + wl.extend_chunk], chan=wl.chan)

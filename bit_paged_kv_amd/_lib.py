@@ -54,6 +54,7 @@ EXPORTED = {
     "nvkv_decode_layers": (_i, [_p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p, _sz, _p]),
     "nvfp4_dequant_to_workspace": (_i, [_p, _p, _p, _p, _f, _f, _p, _i, _p, _p, _i, _i, _i, _i, _i, _f, _f, _p, _p,
                                         _p]),
+    "nvfp4_prefill_write": (_i, [_p, _p, _i, _f, _f, _p, _i, _i, _i, _i, _f, _f, _p, _p, _p, _p, _f, _f, _p, _p, _p]),
     "fp8_workspace_append": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _f, _p, _p, _p]),
     "fp8_extend_attn": (_i, [_p, _p, _p, _p, _p, _p, _f, _f, _f, _i, _i, _i, _i, _i, _i, _p, _p]),
 }
@@ -173,6 +174,31 @@ def prepare_nvfp4_quantize_append(k, v, slots, k_gscale, v_gscale, pool, k_in_sc
     """nvfp4_quantize_append validated and marshalled once; ``run()`` re-issues it (same buffers)."""
     args = _nvfp4_quantize_args(k, v, slots, k_gscale, v_gscale, pool, k_in_scale, v_in_scale)
     return PreparedCall(_lib.nvfp4_kv_quantize_append, args, (k, v, slots, pool), k)
+
+
+def _prefill_args(k, v, slots, k_gscale, v_gscale, pool, k_ws_scale, v_ws_scale, k_ws, v_ws, k_in_scale,
+                  v_in_scale):
+    a = list(_nvfp4_quantize_args(k, v, slots, k_gscale, v_gscale, pool, k_in_scale, v_in_scale))
+    _need(k_ws, torch.uint8, "k_ws")
+    _need(v_ws, torch.uint8, "v_ws")
+    if k_ws.shape != k.shape or v_ws.shape != k.shape:
+        raise ValueError("k_ws, v_ws must be [n_tok][H_kv][128] uint8")
+    return tuple(a[:-1]) + (k_ws_scale, v_ws_scale, _ptr(k_ws), _ptr(v_ws), None)
+
+
+def nvfp4_prefill_write(k, v, slots, k_gscale, v_gscale, pool, k_ws_scale, v_ws_scale, k_ws, v_ws,
+                        k_in_scale: float = 1.0, v_in_scale: float = 1.0):
+    """Quantize-append into the NVFP4 pool and write the FP8 copy the prefill attention reads, in one pass."""
+    args = _prefill_args(k, v, slots, k_gscale, v_gscale, pool, k_ws_scale, v_ws_scale, k_ws, v_ws, k_in_scale,
+                         v_in_scale)
+    _check("nvfp4_prefill_write", _lib.nvfp4_prefill_write(*args[:-1], _stream(k)))
+
+
+def prepare_nvfp4_prefill_write(k, v, slots, k_gscale, v_gscale, pool, k_ws_scale, v_ws_scale, k_ws, v_ws,
+                                k_in_scale: float = 1.0, v_in_scale: float = 1.0):
+    args = _prefill_args(k, v, slots, k_gscale, v_gscale, pool, k_ws_scale, v_ws_scale, k_ws, v_ws, k_in_scale,
+                         v_in_scale)
+    return PreparedCall(_lib.nvfp4_prefill_write, args, (k, v, slots, pool, k_ws, v_ws), k)
 
 
 def fp8_quantize_append(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, k_scale: float, v_scale: float,

@@ -123,7 +123,7 @@ int nvfp4_kv_quantize_append(const void* k_in, const void* v_in, int in_dtype, f
   if (!aligned(k_in, 16) || !aligned(v_in, 16) || !aligned(slots, 4)) return NVKV_E_INVAL;
   if (!aligned(k_data, 16) || !aligned(k_scale, 16) || !aligned(v_data, 16) || !aligned(v_scale, 16))
     return NVKV_E_INVAL;
-  if ((size_t)n_tok * num_kv_heads * 8 > (size_t)0xFFFFFFFF * 256) return NVKV_E_UNSUPPORTED;
+  if (num_kv_heads > 65535) return NVKV_E_UNSUPPORTED;      // one grid row per kv head
   return launch_status(nvkv::launch_nvfp4_quantize(k_in, v_in, in_dtype, k_in_scale, v_in_scale, slots, n_tok,
                                                    num_kv_heads, k_global_scale, v_global_scale, k_data, k_scale,
                                                    v_data, v_scale, stream));
@@ -340,6 +340,32 @@ int nvfp4_dequant_to_workspace(const uint8_t* k_data, const uint8_t* k_scale, co
                                                   page_table, max_pages_per_seq, prefix_lens, ws_offsets, batch,
                                                   num_kv_heads, max_prefix_len, k_ws_scale, v_ws_scale, k_ws, v_ws,
                                                   stream));
+}
+
+int nvfp4_prefill_write(const void* k_in, const void* v_in, int in_dtype, float k_in_scale, float v_in_scale,
+                        const int32_t* slots, int n_tok, int num_kv_heads, int head_dim, int page_size,
+                        float k_global_scale, float v_global_scale, uint8_t* k_data, uint8_t* k_scale,
+                        uint8_t* v_data, uint8_t* v_scale, float k_ws_scale, float v_ws_scale, uint8_t* k_ws,
+                        uint8_t* v_ws, hipStream_t stream) {
+  int st = shape_status(head_dim, page_size);
+  if (st) return st;
+  if (n_tok < 0 || num_kv_heads < 1) return NVKV_E_INVAL;
+  if (in_dtype != NVKV_IN_BF16 && in_dtype != NVKV_IN_FP8_E4M3) return NVKV_E_INVAL;
+  if (!good_scale(k_global_scale) || !good_scale(v_global_scale) || !good_scale(k_ws_scale) ||
+      !good_scale(v_ws_scale))
+    return NVKV_E_INVAL;
+  if (in_dtype == NVKV_IN_FP8_E4M3 && (!good_scale(k_in_scale) || !good_scale(v_in_scale))) return NVKV_E_INVAL;
+  if (n_tok == 0) return NVKV_OK;
+  if (!k_in || !v_in || !slots || !k_data || !k_scale || !v_data || !v_scale || !k_ws || !v_ws) return NVKV_E_INVAL;
+  if (!aligned(k_in, 16) || !aligned(v_in, 16) || !aligned(slots, 4) || !aligned(k_ws, 16) || !aligned(v_ws, 16))
+    return NVKV_E_INVAL;
+  if (!aligned(k_data, 16) || !aligned(k_scale, 16) || !aligned(v_data, 16) || !aligned(v_scale, 16))
+    return NVKV_E_INVAL;
+  if (num_kv_heads > 65535) return NVKV_E_UNSUPPORTED;
+  return launch_status(nvkv::launch_nvfp4_prefill_write(k_in, v_in, in_dtype, k_in_scale, v_in_scale, slots, n_tok,
+                                                        num_kv_heads, k_global_scale, v_global_scale, k_data,
+                                                        k_scale, v_data, v_scale, k_ws_scale, v_ws_scale, k_ws, v_ws,
+                                                        stream));
 }
 
 static int extend_common_status(int batch, int num_kv_heads, int head_dim, int max_chunk_len, int max_prefix_len,

@@ -15,6 +15,10 @@ hipError_t launch_global_scale(const void* x, int in_dtype, float in_scale, size
 hipError_t launch_nvfp4_quantize(const void* k_in, const void* v_in, int in_dtype, float k_in_scale, float v_in_scale,
                                  const int32_t* slots, int n_tok, int hkv, float gk, float gv, uint8_t* k_data,
                                  uint8_t* k_scale, uint8_t* v_data, uint8_t* v_scale, hipStream_t stream);
+hipError_t launch_nvfp4_prefill_write(const void* k_in, const void* v_in, int in_dtype, float k_in_scale,
+                                      float v_in_scale, const int32_t* slots, int n_tok, int hkv, float gk, float gv,
+                                      uint8_t* k_data, uint8_t* k_scale, uint8_t* v_data, uint8_t* v_scale, float sk_ws,
+                                      float sv_ws, uint8_t* k_ws, uint8_t* v_ws, hipStream_t stream);
 hipError_t launch_fp8_quantize(const void* k_in, const void* v_in, const int32_t* slots, int n_tok, int hkv, float sk,
                                float sv, uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream);
 hipError_t launch_dequant_to_ws(const uint8_t* k_data, const uint8_t* k_scale, const uint8_t* v_data,

@@ -117,11 +117,15 @@ constexpr int kQWin = kQTok - 3;          // tokens it owns; the last three are 
 constexpr int kQItems = kQTok * 16;       // (token, block, K|V) items of phase 1
 constexpr int kQThreads = NVKV_Q_THREADS;
 
+// kWs: the prefill write -- every owned token's K and V also go, as E4M3 of fp32(x / s_ws) (the FP8
+// encoding of the mixed-precision layers), to row t of a dense FP8 copy [n_tok][hkv][128] that the
+// prefill attention reads, so the bf16 input is read once for both formats.
+template <bool kWs>
 __global__ __launch_bounds__(kQThreads) void nvfp4_quantize_kernel(
     const uint8_t* __restrict__ k_in, const uint8_t* __restrict__ v_in, int in_dtype, float k_in_scale,
     float v_in_scale, const int32_t* __restrict__ slots, int n_tok, int hkv, float gk, float gv,
     uint8_t* __restrict__ k_data, uint8_t* __restrict__ k_scale, uint8_t* __restrict__ v_data,
-    uint8_t* __restrict__ v_scale) {
+    uint8_t* __restrict__ v_scale, float sk_ws, float sv_ws, uint8_t* __restrict__ k_ws, uint8_t* __restrict__ v_ws) {
   __shared__ uint2 vcodes[kQTok][8];      // [token in window][block]: element i at bits 4 (i % 8) of word i / 8
   __shared__ uint8_t vscales[kQTok][8];
   __shared__ int32_t wslots[kQTok + 3];   // slots of input tokens w0 - 3 .. w0 + kQTok - 1 (-1: none)
@@ -142,6 +146,18 @@ __global__ __launch_bounds__(kQThreads) void nvfp4_quantize_kernel(
     if (t >= n_tok || (!is_v && tr >= kQWin)) continue;
     float x[16];
     load_block16(is_v ? v_in : k_in, in_dtype, is_v ? v_in_scale : k_in_scale, ((size_t)t * hkv + h) * 128 + 16 * j, x);
+    if constexpr (kWs) {
+      if (tr < kQWin) {
+        const float s = is_v ? sv_ws : sk_ws;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = e4m3_encode(x[4 * i] / s) | (e4m3_encode(x[4 * i + 1] / s) << 8) |
+                 (e4m3_encode(x[4 * i + 2] / s) << 16) | (e4m3_encode(x[4 * i + 3] / s) << 24);
+        *reinterpret_cast<uint4*>((is_v ? v_ws : k_ws) + ((size_t)t * hkv + h) * 128 + 16 * j) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
     uint32_t lo, hi;
     const uint32_t sc = nvfp4_quantize_block_packed(x, is_v ? gv : gk, lo, hi);
     if (is_v) {
@@ -462,8 +478,20 @@ hipError_t launch_nvfp4_quantize(const void* k_in, const void* v_in, int in_dtyp
                                  const int32_t* slots, int n_tok, int hkv, float gk, float gv, uint8_t* k_data,
                                  uint8_t* k_scale, uint8_t* v_data, uint8_t* v_scale, hipStream_t stream) {
   dim3 grid((unsigned)(((size_t)n_tok + kQWin - 1) / kQWin), hkv);
-  hipLaunchKernelGGL(nvfp4_quantize_kernel, grid, dim3(kQThreads), 0, stream, (const uint8_t*)k_in, (const uint8_t*)v_in,
-                     in_dtype, k_in_scale, v_in_scale, slots, n_tok, hkv, gk, gv, k_data, k_scale, v_data, v_scale);
+  hipLaunchKernelGGL(nvfp4_quantize_kernel<false>, grid, dim3(kQThreads), 0, stream, (const uint8_t*)k_in,
+                     (const uint8_t*)v_in, in_dtype, k_in_scale, v_in_scale, slots, n_tok, hkv, gk, gv, k_data, k_scale,
+                     v_data, v_scale, 1.0f, 1.0f, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_prefill_write(const void* k_in, const void* v_in, int in_dtype, float k_in_scale,
+                                      float v_in_scale, const int32_t* slots, int n_tok, int hkv, float gk, float gv,
+                                      uint8_t* k_data, uint8_t* k_scale, uint8_t* v_data, uint8_t* v_scale, float sk_ws,
+                                      float sv_ws, uint8_t* k_ws, uint8_t* v_ws, hipStream_t stream) {
+  dim3 grid((unsigned)(((size_t)n_tok + kQWin - 1) / kQWin), hkv);
+  hipLaunchKernelGGL(nvfp4_quantize_kernel<true>, grid, dim3(kQThreads), 0, stream, (const uint8_t*)k_in,
+                     (const uint8_t*)v_in, in_dtype, k_in_scale, v_in_scale, slots, n_tok, hkv, gk, gv, k_data, k_scale,
+                     v_data, v_scale, sk_ws, sv_ws, k_ws, v_ws);
   return hipGetLastError();
 }
 

@@ -244,6 +244,23 @@ NVKV_API int nvfp4_dequant_to_workspace(const uint8_t* k_data, const uint8_t* k_
                                uint8_t* k_ws, uint8_t* v_ws, hipStream_t stream);
 
 /*
+ * nvfp4_prefill_write -- the prefill path's single-pass write ([S] "Three Paths" paragraph 1 and
+ * summary bullet 2: prefill quantizes K/V into the persistent NVFP4 cache and attends with BF16 Q
+ * against FP8 K/V, without reading the cache): nvfp4_kv_quantize_append, plus every token's K and V
+ * as E4M3_rne_sat(fp32(x / ws_scale)) in row t (input order) of a dense FP8 copy that
+ * fp8_extend_attn reads with prefix_lens = 0 and ws_offsets = the token offsets of each sequence.
+ *   k_ws, v_ws : [n_tok][num_kv_heads][128] E4M3, device, 16-byte aligned.
+ * Other arguments, errors and the no-op at n_tok == 0 as nvfp4_kv_quantize_append, plus bad
+ * ws scales (NVKV_E_INVAL).
+ */
+NVKV_API int nvfp4_prefill_write(const void* k_in, const void* v_in, int in_dtype,
+                        float k_in_scale, float v_in_scale, const int32_t* slots, int n_tok,
+                        int num_kv_heads, int head_dim, int page_size,
+                        float k_global_scale, float v_global_scale,
+                        uint8_t* k_data, uint8_t* k_scale, uint8_t* v_data, uint8_t* v_scale,
+                        float k_ws_scale, float v_ws_scale, uint8_t* k_ws, uint8_t* v_ws, hipStream_t stream);
+
+/*
  * fp8_workspace_append -- the extend chunk's own K/V join its prefix in the FP8 workspace ([S]
  * "Three Paths" paragraph 2: the extend attention runs over prefix || chunk in FP8):
  *     w = E4M3_rne_sat(fp32(x / ws_scale)), x the bf16 value (the FP8 encoding of the mixed-precision

@@ -30,7 +30,7 @@ def _declared():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib._lib, n), f"{n} not exported by libnvkv.so"
         assert n in lib.EXPORTED, f"{n} has no binding"
@@ -210,3 +210,17 @@ def test_extend_validation(lib):
                        (4, None, INVAL)):
         a = list(base); a[i] = v
         assert ex(*a) == want, (i, v)
+
+
+def test_prefill_write_validation(lib):
+    pw = lib._lib.nvfp4_prefill_write
+    #       k  v  dt  ks   vs   slots n  hkv D    page g_k  g_v  kd ks vd vs  sk_ws sv_ws k_ws v_ws stream
+    base = [A, A, 0,  1.0, 1.0, A,    4, 2,  128, 16,  1.0, 1.0, A, A, A, A,  1.0,  1.0,  A,   A,   S]
+    ok0 = list(base); ok0[6] = 0
+    assert pw(*ok0) == OK                                 # nothing to write: no launch
+    for i, v, want in ((0, None, INVAL), (0, MIS, INVAL), (2, 7, INVAL), (5, A + 2, INVAL), (6, -1, INVAL),
+                       (7, 0, INVAL), (7, 70000, UNSUP), (8, 64, UNSUP), (9, 32, UNSUP), (10, 0.0, INVAL),
+                       (16, 0.0, INVAL), (17, float("nan"), INVAL), (18, None, INVAL), (19, MIS, INVAL),
+                       (15, None, INVAL)):
+        a = list(base); a[i] = v
+        assert pw(*a) == want, (i, v)

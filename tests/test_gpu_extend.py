@@ -227,3 +227,39 @@ def test_extend_full_size_sampled(nv):
     want = np.stack([o_att.decode_attention_one(qn[i], k_hat[:prefix + i + 1], v_hat[:prefix + i + 1], wl.sm_scale)
                      for i in rows])
     H.assert_attention_close(got[rows], want, "extend full size, sampled rows")
+
+
+@pytest.mark.parametrize("lens", [[5], [300, 1, 77, 64]])
+def test_prefill_write_and_attention(nv, lens):
+    """The prefill path: one pass writes the NVFP4 cache (bytes as the oracle's quantize-append) and
+    the dense FP8 copy (bytes as the oracle's FP8 quantize); the causal attention over that copy
+    (prefix 0) matches the fp64 oracle.  Sequences start at arbitrary token quads (misaligned runs)."""
+    wl = workloads.Workload(name="prefill-small", seed=33, batch=len(lens), h_kv=2, h_q=8, seq_lens=lens,
+                            chan="outlier2", extra_pages=2)
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    s_wk, s_wv = np.float32(6.0) * gk, np.float32(6.0) * gv
+    want_pool = H.oracle_nvfp4_pool(wl, ks, vs, gk, gv)
+    k_all, v_all = np.concatenate(ks), np.concatenate(vs)
+    want_kw, want_vw = o_fp8.fp8_quantize(k_all, s_wk), o_fp8.fp8_quantize(v_all, s_wv)
+    k, v, slots = H.gpu_all_tokens(wl, 0, DEV)
+    pool = nv.alloc_nvfp4_pool(wl.num_pages, wl.h_kv, DEV)
+    kw = torch.full(k.shape, 0x11, dtype=torch.uint8, device=DEV)
+    vw = kw.clone()
+    nv.nvfp4_prefill_write(k, v, slots, float(gk), float(gv), pool, float(s_wk), float(s_wv), kw, vw)
+    torch.cuda.synchronize()
+    for key in ("k_data", "k_scale", "v_data", "v_scale"):
+        assert np.array_equal(pool[key].cpu().numpy(), want_pool[key]), key
+    assert np.array_equal(kw.cpu().numpy(), want_kw)
+    assert np.array_equal(vw.cpu().numpy(), want_vw)
+    # prefill attention: chunk = the whole sequence, prefix 0, workspace rows = token offsets
+    rng = np.random.default_rng(8)
+    q = _bf16(rng.standard_normal((k_all.shape[0], wl.h_q, 128))).float().numpy()
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    prefixes = [0] * len(lens)
+    want = _oracle(q, want_kw, want_vw, s_wk, s_wv, offs, offs, prefixes, wl.sm_scale)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    out = nv.fp8_extend_attn(_bf16(q).to(DEV), t(offs), kw, vw, t(offs), t(np.zeros(len(lens), np.int32)),
+                             float(s_wk), float(s_wv), wl.sm_scale, wl.h_kv, max(lens), 0)
+    torch.cuda.synchronize()
+    H.assert_attention_close(out.cpu().numpy(), want, f"prefill {lens}")
