@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="long", choices=["long", "batch32", "ragged", "mixed", "extend", "prefill",
-                                                         "tiny"])
+                                                         "tiny", "sweep"])
     ap.add_argument("--pages-per-split", type=int, default=0, help="force the split size (0 = planner)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -173,6 +173,37 @@ def cpu_baseline(cfg_index, budget_s=6.0):
 
 
 # ------------------------------------------------------------------------------------------------
+def precision_studies(nv, workloads, dev):
+    """The per-layer NVFP4-vs-FP8 sensitivity sweep over the 28-layer stack's synthetic K/V (batch 4
+    x 8192 tokens, the stack's per-layer channel scales and outlier channels), and the per-tensor
+    scale variants on one layer; prints one JSON line."""
+    import torch
+    from bit_paged_kv_amd import analysis
+    base = workloads.config(4)
+    wl = workloads.Workload(name="sweep", seed=base.seed, batch=4, h_kv=base.h_kv, h_q=base.h_q,
+                            seq_lens=[8192] * 4, chan=base.chan, layers=base.layers, fp8_layers=base.fp8_layers)
+    pt = torch.from_numpy(wl.page_table).to(dev)
+    sl = torch.from_numpy(wl.total_lens.astype(np.int32)).to(dev)
+    slots = torch.from_numpy(np.concatenate([wl.slots(b) for b in range(wl.batch)])).to(dev)
+    t0 = time.perf_counter()
+    rows = []
+    for layer in range(wl.layers):
+        k = torch.cat([wl.kv("k", b, layer) for b in range(wl.batch)]).to(dev)
+        v = torch.cat([wl.kv("v", b, layer) for b in range(wl.batch)]).to(dev)
+        L = {"q": wl.q(layer).to(dev), "k": k, "v": v}
+        r = analysis.layer_sensitivity([L], slots, wl.num_pages, pt, sl, wl.sm_scale, wl.h_kv)[0]
+        r["layer"] = layer
+        rows.append(r)
+        if layer == 1:
+            variants = analysis.gscale_variants(L["q"], k, v, slots, wl.num_pages, pt, sl, wl.sm_scale, wl.h_kv,
+                                                calib_tokens=1024)
+        log(f"layer {layer}: NVFP4 vs FP8 rel-L2 {r['nvfp4_vs_fp8']['rel_l2']:.3e}, {time.perf_counter() - t0:.1f} s")
+    order = sorted(range(len(rows)), key=lambda i: -rows[i]["nvfp4_vs_bf16"]["rel_l2"])
+    print(json.dumps({"study": "per-layer NVFP4 sensitivity and per-tensor scale variants",
+                      "data": "synthetic (seeded; 28-layer stack's per-layer channel scales, batch 4 x 8192)",
+                      "layers": rows, "most_sensitive_first": order, "gscale_variants_layer1": variants}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -190,6 +221,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     name = args.config
+    if name == "sweep":
+        precision_studies(nv, workloads, dev)
+        return
     index = {"tiny": 0, "batch32": 1, "long": 2, "ragged": 3, "mixed": 4, "extend": 4, "prefill": 4}[name]
     wl = workloads.config(index)
     stream = torch.cuda.current_stream(dev)
