@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark: NVFP4 paged decode attention on one MI355X -- effective KV GB/s (% of HBM peak) + tokens/s.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long|batch32|ragged|mixed|extend|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long|batch32|ragged|mixed|extend|prefill|tiny|sweep]
 
 One step is one decode step of the workload's hot path, inputs already resident in HBM:
   long     split-K NVFP4 decode + log-sum-exp merge, 4 x 131072 tokens, 8 KV / 64 query heads (default)
@@ -11,10 +11,15 @@ One step is one decode step of the workload's hot path, inputs already resident 
   mixed    28 layers, FP8 at layers 0, 25, 26, 27 and NVFP4 elsewhere, 44 x 8192 tokens
   extend   per NVFP4 layer of the mixed stack: 16384-token prefix -> FP8 workspace + 2048-token
            chunk quantize-append (24 layers per step)
+  prefill  per NVFP4 layer: one-pass NVFP4 cache + FP8 copy write of a prompt and causal attention
+           over the copy
   tiny     1 x 256 tokens (latency-bound)
+  sweep    precision studies (per-layer NVFP4 vs FP8 sensitivity, per-tensor scale variants)
 
-The timed region is exactly K steps between two device synchronisations; per-step GPU time of the
-decode launches is also taken with HIP events recorded on the launch stream.  Effective KV GB/s =
+The timed region is exactly K steps between two device synchronisations.  The decode kernel's own
+duration comes from HIP events that its dispatch records on every 5th timed step (a recorded
+dispatch adds a few microseconds to its step); extend and prefill time each attention launch with
+events on the launch stream.  Effective KV GB/s =
 NVFP4 (or FP8) bytes the step must read (144 B per token and KV head; 256 B for FP8) / step time.
 The CPU baseline times the fp64 oracle (dequantize + attention, one thread) on a bounded sample.
 """
@@ -36,8 +41,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 / fp16 matrix-core peak of MI355X
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="long", choices=["long", "batch32", "ragged", "mixed", "extend", "prefill",
                                                          "tiny", "sweep"])
     ap.add_argument("--pages-per-split", type=int, default=0, help="force the split size (0 = planner)")
@@ -76,6 +81,8 @@ class HipEventPairs:
             self.hip.hipEventDestroy(e)
 
 
+EVENT_EVERY = 5     # decode configs: timed steps per dispatch-recorded kernel duration
+
 # HBM traffic of decode_split_kernel on the long workload, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives (x2.000 / x1.000).  Valid only
 # for the kernel source they were taken with; reported as null for any other source.
@@ -90,6 +97,28 @@ def decode_source_sha256():
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_paged_kv_amd", "csrc", "nvkv_decode.hip")
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
+
+
+def stream_read_ceiling(nv, nbytes, dev, reps=20):
+    """Streaming-read rate of the device in GB/s: the library's read probe (coalesced 16-byte loads
+    over the whole GPU) on a buffer of max(nbytes, 768 MiB) -- larger than the 256 MB last-level
+    cache -- timed with events on the launch stream around each of `reps` launches."""
+    import torch
+    n = max(int(nbytes), 768 << 20) // 16 * 16
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)     # every 16-byte chunk folds to 0
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(5):
+        nv.read_probe(buf, sink)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in pairs:
+        e0.record()
+        nv.read_probe(buf, sink)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in pairs) / reps
+    del buf
+    return {"value": round(n / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "bytes": n, "us_per_read": round(ms * 1e3, 2),
+            "method": f"nvkv_read_probe, mean of {reps} launches"}
 
 
 # ------------------------------------------------------------------------------------------------
@@ -421,11 +450,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # the split kernel's own dispatch records one event pair per step (no commands are added to
-    # the stream); the step as a whole is bracketed by device synchronisations
+    # the split kernel's own dispatch records an event pair on every EVENT_EVERY-th timed step (no
+    # commands are added to the stream; a recorded dispatch costs the step a few microseconds, so
+    # not every step records); the step as a whole is bracketed by device synchronisations
     events = None
+    event_every = 1
     if timed_kernel and timed_kernel.startswith("decode_split_kernel"):
-        events = HipEventPairs(args.steps)
+        event_every = EVENT_EVERY
+        events = HipEventPairs((args.steps + event_every - 1) // event_every)
     elif timed_kernel == "extend_attn_kernel":
         events = True          # the step records torch events around each attention launch
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -434,7 +466,10 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        step(events, i)
+        if i % event_every == 0:
+            step(events, i // event_every)
+        else:
+            step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -454,8 +489,9 @@ def main():
         events.close()
         kernel_ms = sum(kms) / len(kms)
         achieved = kernel_bytes / (kernel_ms * 1e-3) / 1e9
-        timing = (f"{timed_kernel}: mean of {len(kms)} per-launch durations (min {min(kms) * 1e3:.1f} us, max "
-                  f"{max(kms) * 1e3:.1f} us) from hipEvents its dispatch recorded on the launch stream")
+        timing = (f"{timed_kernel}: mean of {len(kms)} per-launch durations (every {event_every}th of the "
+                  f"{args.steps} timed steps; min {min(kms) * 1e3:.1f} us, max {max(kms) * 1e3:.1f} us) from "
+                  f"hipEvents its dispatch recorded on the launch stream")
     else:
         kernel_ms = step_gpu_ms
         achieved = step_bytes / (kernel_ms * 1e-3) / 1e9
@@ -466,6 +502,13 @@ def main():
     log(f"{args.steps} steps: wall {ms_per_step:.4f} ms/step, events {step_gpu_ms:.4f} ms/step, "
         f"{value:.1f} GB/s ({value / HBM_PEAK_GBS:.1%} of 8 TB/s); {timed_kernel} {kernel_ms * 1e3:.1f} us "
         f"-> {achieved:.1f} {unit} ({achieved / peak:.1%} of {peak:.0f})")
+
+    # the device's streaming-read rate, for the decode configs (after the timed region)
+    ceiling = None
+    if bound == "hbm":
+        ceiling = stream_read_ceiling(nv, step_bytes if name != "mixed" else wl.kv_bytes_nvfp4(), dev)
+        log(f"streaming-read ceiling {ceiling['value']} GB/s; step at {100.0 * value / ceiling['value']:.1f} %, "
+            f"kernel at {100.0 * achieved / ceiling['value']:.1f} % of it")
 
     cpu = None
     if not args.no_cpu_baseline and name in ("long", "batch32", "ragged", "tiny"):
@@ -509,6 +552,10 @@ def main():
                      "traffic_detail": traffic_detail, "timing": timing},
         "cpu_baseline": cpu,
     }
+    if ceiling is not None:
+        res["stream_read_ceiling"] = ceiling
+        res["pct_of_stream_read_ceiling"] = round(100.0 * value / ceiling["value"], 2)
+        res["roofline"]["frac_of_stream_read_ceiling"] = round(achieved / ceiling["value"], 4)
     print(json.dumps(res), flush=True)
 
 

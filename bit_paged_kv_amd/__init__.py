@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     fp8_workspace_append, global_scale, prepare_fp8_extend_attn, prepare_fp8_workspace_append,
     nvfp4_decode, nvfp4_pool_bytes, nvfp4_prefill_write, nvfp4_quantize_append, plan_decode, prepare_decode_layers,
     prepare_nvfp4_prefill_write,
-    prepare_dequant_to_workspace, prepare_nvfp4_decode, prepare_nvfp4_quantize_append, status_string, version,
+    prepare_dequant_to_workspace, prepare_nvfp4_decode, prepare_nvfp4_quantize_append, read_probe, status_string,
+    version,
     PreparedCall, PreparedDecode,
 )

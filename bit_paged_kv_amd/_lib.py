@@ -57,6 +57,7 @@ EXPORTED = {
     "nvfp4_prefill_write": (_i, [_p, _p, _i, _f, _f, _p, _i, _i, _i, _i, _f, _f, _p, _p, _p, _p, _f, _f, _p, _p, _p]),
     "fp8_workspace_append": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _f, _p, _p, _p]),
     "fp8_extend_attn": (_i, [_p, _p, _p, _p, _p, _p, _f, _f, _f, _i, _i, _i, _i, _i, _i, _p, _p]),
+    "nvkv_read_probe": (_i, [_p, _sz, _p, _p]),
 }
 for _name, (_res, _args) in EXPORTED.items():
     _fn = getattr(_lib, _name)
@@ -478,3 +479,14 @@ def prepare_fp8_extend_attn(q, chunk_offsets, k_ws, v_ws, ws_offsets, prefix_len
 
 def default_sm_scale() -> float:
     return 1.0 / math.sqrt(HEAD_DIM)
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Measurement helper (nvkv_read_probe): read every byte of the contiguous GPU tensor ``buf``
+    once with coalesced 16-byte loads.  ``sink`` is a GPU int32 tensor that receives 0x9E3779B9
+    only if a thread's xor fold of its words equals that value."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _need(sink, torch.int32, "sink")
+    nbytes = buf.numel() * buf.element_size()
+    _check("nvkv_read_probe", _lib.nvkv_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(buf)))

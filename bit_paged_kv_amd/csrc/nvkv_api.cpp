@@ -414,4 +414,13 @@ int fp8_extend_attn(const void* q, const int32_t* chunk_offsets, const uint8_t* 
                                                 max_chunk_len, out, stream));
 }
 
+int nvkv_read_probe(const void* buf, size_t bytes, unsigned* sink, hipStream_t stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 != 0) return NVKV_E_INVAL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return NVKV_E_INVAL;
+  const int cus = device_cus();
+  if (cus < 1) return NVKV_E_LAUNCH;
+  // eight workgroups of 256 threads per compute unit: the fastest grid-stride shape measured
+  return launch_status(nvkv::launch_read_probe(buf, bytes, sink, 8 * cus, stream));
+}
+
 }  // extern "C"

@@ -64,4 +64,7 @@ size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start = nullptr,
                          hipEvent_t stop = nullptr);
 
+// Streaming-read probe over `bytes` (a multiple of 16) with `workgroups` workgroups of 256 threads.
+hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, int workgroups, hipStream_t stream);
+
 }  // namespace nvkv

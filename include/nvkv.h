@@ -304,6 +304,19 @@ NVKV_API int fp8_extend_attn(const void* q, const int32_t* chunk_offsets,
                     int batch, int num_q_heads, int num_kv_heads, int head_dim,
                     int max_chunk_len, int max_prefix_len, float* out, hipStream_t stream);
 
+/*
+ * nvkv_read_probe -- measurement helper, not part of the attention path: reads `bytes` bytes at
+ * `buf` once with coalesced 16-byte loads spread over the whole device (eight 256-thread
+ * workgroups per compute unit, grid-stride).  Each thread folds its words by xor and writes the
+ * fold to *sink only if it equals 0x9E3779B9, so the loads cannot be elided and normally nothing
+ * is written.  Timing it gives the streaming-read rate of the device, the practical ceiling for
+ * the decode's reads (the quoted HBM peak is not reached by any read pattern).
+ *   buf   : device, 16-byte aligned; bytes >= 16 and a multiple of 16.
+ *   sink  : device, 4 bytes, 4-byte aligned.
+ * Errors: NVKV_E_INVAL for a null pointer, misalignment or a bad size; NVKV_E_LAUNCH.
+ */
+NVKV_API int nvkv_read_probe(const void* buf, size_t bytes, unsigned* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

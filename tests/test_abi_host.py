@@ -30,7 +30,7 @@ def _declared():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib._lib, n), f"{n} not exported by libnvkv.so"
         assert n in lib.EXPORTED, f"{n} has no binding"
@@ -224,3 +224,14 @@ def test_prefill_write_validation(lib):
                        (15, None, INVAL)):
         a = list(base); a[i] = v
         assert pw(*a) == want, (i, v)
+
+
+def test_read_probe_validation(lib):
+    p = lib._lib.nvkv_read_probe
+    assert p(None, 32, A, S) == INVAL
+    assert p(A, 32, None, S) == INVAL
+    assert p(A, 0, A, S) == INVAL
+    assert p(A, 15, A, S) == INVAL
+    assert p(A, 40, A, S) == INVAL          # not a multiple of 16
+    assert p(MIS, 32, A, S) == INVAL
+    assert p(A, 32, A + 2, S) == INVAL      # sink not 4-byte aligned
