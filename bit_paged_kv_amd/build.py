@@ -7,10 +7,11 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvkv.so")
-# per-source extra flags.  The decode kernels never see NaN scores (masked tokens are -inf and
-# their scales are zeroed), so their max trees need no NaN quieting; the write-side kernels keep
-# strict IEEE semantics for bit-exact quantization.
-SOURCES = {"nvkv_quant.hip": [], "nvkv_decode.hip": ["-fno-honor-nans"], "nvkv_extend.hip": [], "nvkv_probe.hip": [],
+# per-source extra flags.  The decode and extend-attention kernels never see NaN scores (masked
+# keys are -inf, unwritten scales are zeroed), so their max trees need no NaN quieting; the
+# write-side kernels keep strict IEEE semantics for bit-exact quantization.
+SOURCES = {"nvkv_quant.hip": [], "nvkv_decode.hip": ["-fno-honor-nans"], "nvkv_extend.hip": [],
+           "nvkv_extend_attn.hip": ["-fno-honor-nans"], "nvkv_probe.hip": [],
            "nvkv_api.cpp": []}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
