@@ -75,6 +75,9 @@ def _gpu(nv, q, k_ws, v_ws, sk, sv, ws_off, c_off, prefixes, sm, hkv):
     ([64], [64], 1, 16),                         # G = 16: 8 tokens per workgroup
     ([100, 0], [45, 17], 4, 4),                  # G = 1
     ([31], [96], 3, 6),                          # G = 2, tile and workgroup edges
+    ([130], [200], 1, 3),                        # G = 3: 85 tokens per workgroup, one padding column
+    ([9], [90], 2, 14),                          # G = 7: 36 tokens per workgroup, four padding columns
+    ([250, 40], [33, 70], 2, 16),                # G = 8: 32 tokens per workgroup
 ])
 def test_extend_attention_matches_oracle(nv, prefixes, chunks, hkv, hq):
     sm = 1.0 / np.sqrt(128.0)
@@ -82,6 +85,27 @@ def test_extend_attention_matches_oracle(nv, prefixes, chunks, hkv, hq):
     want = _oracle(*args, prefixes, sm)
     got = _gpu(nv, *args, prefixes, sm, hkv)
     H.assert_attention_close(got, want, f"extend p={prefixes} c={chunks} G={hq // hkv}")
+
+
+def test_extend_attention_rising_maximum(nv):
+    """K rows grow ~12x along the sequence, so the running maximum of every column rises again and
+    again (each rise rescales the accumulated output); 100 chunk tokens at G = 4 fill both halves of
+    a workgroup's columns."""
+    prefixes, chunks, hkv, hq = [500], [100], 2, 8
+    rng = np.random.default_rng(77)
+    rows = prefixes[0] + chunks[0]
+    kx = rng.standard_normal((rows, hkv, 128)).astype(np.float32) * np.linspace(1.0, 12.0, rows)[:, None, None]
+    vx = rng.standard_normal((rows, hkv, 128)).astype(np.float32)
+    sk, sv = o_fp8.fp8_scale(kx), o_fp8.fp8_scale(vx)
+    k_ws, v_ws = o_fp8.fp8_quantize(kx, sk), o_fp8.fp8_quantize(vx, sv)
+    ws_off = np.array([0, rows], dtype=np.int32)
+    c_off = np.array([0, chunks[0]], dtype=np.int32)
+    q = _bf16(rng.standard_normal((chunks[0], hq, 128))).float().numpy()
+    sm = 1.0 / np.sqrt(128.0)
+    args = (q, k_ws, v_ws, sk, sv, ws_off, c_off)
+    want = _oracle(*args, prefixes, sm)
+    got = _gpu(nv, *args, prefixes, sm, hkv)
+    H.assert_attention_close(got, want, "extend, rising maximum")
 
 
 def test_extend_attention_repeatable_and_prepared(nv):
