@@ -293,9 +293,11 @@ NVKV_API int fp8_workspace_append(const void* k, const void* v, const int32_t* c
  *                   and fp8_workspace_append).
  *   out           : [total_chunk][num_q_heads][128] fp32, device; every row of every chunk is written.
  *   max_chunk_len, max_prefix_len : host upper bounds of the chunk lengths and prefix_lens.
- * Computed with bf16 q x bf16 K (exact from E4M3) on the matrix cores, fp32 scores, fp16 softmax
- * weights x fp16 V (exact from E4M3), fp32 accumulation.  Errors as fp8_workspace_append, plus
- * NVKV_E_INVAL / NVKV_E_UNSUPPORTED for the head counts (as the decode calls) and a bad sm_scale.
+ * Computed with bf16 q x bf16 K (exact from E4M3) on the matrix cores, fp32 scores, softmax weights
+ * as an fp16 hi + lo pair x fp16 V (exact from E4M3), fp32 accumulation.  The workspace rows a call
+ * reads must hold no E4M3 NaN byte (0x7F, 0xFF; the library's writers produce none from finite
+ * inputs), and q must be finite.  Errors as fp8_workspace_append, plus NVKV_E_INVAL /
+ * NVKV_E_UNSUPPORTED for the head counts (as the decode calls) and a bad sm_scale.
  */
 NVKV_API int fp8_extend_attn(const void* q, const int32_t* chunk_offsets,
                     const uint8_t* k_ws, const uint8_t* v_ws,
