@@ -85,10 +85,11 @@ EVENT_EVERY = 5     # decode configs: timed steps per dispatch-recorded kernel d
 
 # HBM traffic of decode_split_kernel on the long workload, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives (x2.000 / x1.000).  Valid only
-# for the kernel source they were taken with; reported as null for any other source.
+# for the kernel source and the split plan they were taken with; reported as null otherwise.
 TRAFFIC = {
     "long": {"source_sha256": "6dcd6113121cfd45865aa21931858a7b8e8111b2882d0174adbeca859244a5e1",
-             "fetch_kib": 296363.4, "write_kib": 3268.6, "fetch_factor": 2.0, "write_factor": 1.0},
+             "plan": [512, 16], "fetch_kib": 296024.8, "write_kib": 2203.9, "fetch_factor": 2.0,
+             "write_factor": 1.0},
 }
 
 
@@ -518,7 +519,7 @@ def main():
     traffic, traffic_detail = None, None
     t = TRAFFIC.get(name)
     if t is not None and timed_kernel.startswith("decode_split_kernel"):
-        if decode_source_sha256() == t["source_sha256"]:
+        if decode_source_sha256() == t["source_sha256"] and list(plan) == t["plan"]:
             rd = t["fetch_kib"] * 1024 * t["fetch_factor"]
             wr = t["write_kib"] * 1024 * t["write_factor"]
             traffic = round(rd + wr)
@@ -526,7 +527,7 @@ def main():
                               "algorithmic_read_bytes": kernel_bytes,
                               "source": "rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE per dispatch x copy calibration"}
         else:
-            traffic_detail = "kernel source changed since the counters were taken"
+            traffic_detail = "kernel source or split plan changed since the counters were taken"
     res = {
         "metric": "NVFP4 paged decode attn: effective KV GB/s (% of HBM peak) + tokens/s",
         "value": round(value, 2),

@@ -151,21 +151,34 @@ int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long tot
       !pages_per_split || !num_splits)
     return NVKV_E_INVAL;
   const long long max_pages = (max_seq_len + kPage - 1) / kPage;
-  long long pps;
+  long long pps = 0;
   if (force_pages_per_split > 0) {
     pps = force_pages_per_split;
   } else {
-    // page-heads of the whole step spread over ~3 four-wave workgroups per compute unit (the
-    // decode kernel's occupancy)
-    const long long seq_pages = total_tokens > 0 ? (total_tokens + (long long)batch * (kPage - 1)) / kPage
-                                                 : (long long)batch * max_pages;
-    const long long work = seq_pages * num_kv_heads;
-    long long target = (long long)device_cus() * 3;
-    // ragged batch (lengths known to differ): smaller splits, so that the hardware can hand the
-    // splits of short sequences to compute units that finished early
-    if (total_tokens > 0 && total_tokens * 10 < (long long)batch * max_seq_len * 9) target = target * 3 / 2;
-    pps = std::max<long long>(8, (work + target - 1) / target);
-    pps = (pps + 7) & ~7LL;                             // whole pairs of pages for each of the 4 waves
+    const long long cus = device_cus();
+    const long long streams = (long long)batch * num_kv_heads;
+    // ragged batch (lengths known to differ from the longest)
+    const bool ragged = total_tokens > 0 && total_tokens * 10 < (long long)batch * max_seq_len * 9;
+    // Equal lengths and a stream count that divides two workgroups per compute unit: exactly two
+    // per unit, the fastest shape measured (long contexts, 32 streams x 16 splits: 116-118 us
+    // against 119-120 us at three per unit; 32 x 4096, 256 streams x 2: 34.5 against 36 us),
+    // while splits stay at least 64 pages long.
+    if (!ragged && (2 * cus) % streams == 0) {
+      const long long splits2 = 2 * cus / streams;
+      const long long p2 = (((max_pages + splits2 - 1) / splits2) + 7) & ~7LL;
+      if (p2 >= 64) pps = p2;
+    }
+    if (pps == 0) {
+      // otherwise the page-heads of the step spread over ~3 workgroups per unit (the kernel's
+      // occupancy; an uneven 2.75 per unit measured slower), or 4.5 for a ragged batch, so that
+      // the hardware can hand the splits of short sequences to units that finished early
+      const long long seq_pages = total_tokens > 0 ? (total_tokens + (long long)batch * (kPage - 1)) / kPage
+                                                   : (long long)batch * max_pages;
+      const long long work = seq_pages * num_kv_heads;
+      const long long target = ragged ? cus * 9 / 2 : cus * 3;
+      pps = std::max<long long>(8, (work + target - 1) / target);
+      pps = (pps + 7) & ~7LL;                           // whole pairs of pages for each of the 4 waves
+    }
   }
   pps = (pps + 1) & ~1LL;
   pps = std::min<long long>(pps, std::max<long long>(2, (max_pages + 1) & ~1LL));

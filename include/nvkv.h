@@ -123,7 +123,9 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
  * each (sequence, kv head, split) is one workgroup of four wavefronts (each takes a contiguous
  * quarter of the split and the four combine in LDS); with several splits a second kernel merges the
  * partial softmax states.
- * nvkv_plan_decode picks num_splits from host-side hints so that the grid fills the GPU:
+ * nvkv_plan_decode picks num_splits from host-side hints so that the grid fills the GPU (exactly
+ * two workgroups per compute unit when the lengths are equal and the stream count batch *
+ * num_kv_heads allows it, else about three, or 4.5 for a ragged batch):
  *   max_seq_len  : the longest sequence (tokens, including an appended token), > 0.
  *   total_tokens : sum of sequence lengths if known, else 0 (then batch * max_seq_len is assumed).
  *   force_pages_per_split : > 0 forces the split size (rounded up to even); 0 = automatic.
