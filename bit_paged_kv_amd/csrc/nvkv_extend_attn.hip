@@ -387,7 +387,8 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
   else
     store_v(0);
   load_stage(1);
-  // nothing older than tile 1's loads is in flight when the loops start (the q loads included)
+  // nothing is in flight when the loops start (the q loads and tile 1's loads included), so the
+  // loops' only memory waits are the ones their own prefetches need
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
   if (group_a) {
