@@ -11,6 +11,8 @@ import re
 
 import pytest
 
+import workloads
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvkv.h")
 
@@ -56,6 +58,18 @@ def test_plan_covers_the_longest_sequence(lib, b, hkv, L, tot):
     assert pps >= 2 and pps % 2 == 0 and ns >= 1
     assert ns * pps >= pages
     assert (ns - 1) * pps < pages          # no split starts past the end of the longest sequence
+
+
+def test_plan_shapes(lib):
+    """The planner's shapes on a 256-CU device (the count it assumes without a GPU, and MI355X's):
+    exactly two workgroups per CU when the stream count divides 512 and the lengths are equal,
+    about three otherwise, 4.5 for a ragged batch."""
+    assert lib.plan_decode(4, 8, 131072, 4 * 131072) == (512, 16)      # 32 streams x 16 = 512
+    assert lib.plan_decode(32, 8, 4096, 32 * 4096) == (128, 2)         # 256 streams x 2 = 512
+    assert lib.plan_decode(44, 8, 8192, 44 * 8192) == (240, 3)         # 352 streams: ~3 per CU
+    rag = workloads.config(3)                                          # ragged: ~4.5 per CU
+    assert lib.plan_decode(rag.batch, rag.h_kv, int(rag.total_lens.max()), int(rag.total_lens.sum())) == (216, 10)
+    assert lib.plan_decode(1, 1, 256, 256) == (8, 2)                   # short: splits stay >= 8 pages
 
 
 def test_plan_forced_split(lib):
