@@ -40,6 +40,38 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | code;
 }
 
+// E4M3 bytes of fp32(x[i] / s) for four values (byte i of the result), bit-identical to
+// e4m3_encode(x[i] / s) for every input; r = fp32(1 / s).
+//  * q = x * r lies within 3 ulp of fp32(x / s).  The two can round to different E4M3 values only
+//    next to a rounding midpoint of the normal range (fraction bits 19..0 near 0x80000), in the
+//    subnormal range (0 < |q| < 2^-6, where the rounding position moves with the exponent), or when
+//    x * r is NaN (x NaN, or 0 * inf for a tiny s).  A lane in any of these cases divides.
+//  * gfx950's v_cvt_scalef32_pk_fp8_f32 with scale 1.0 rounds exactly like e4m3_encode for every
+//    input of magnitude below 448 (compared on all 2^32 fp32 patterns); it does not saturate, so the
+//    magnitude is clamped to 448 first, and fmin(NaN, 448) = 448 with the sign kept reproduces the
+//    encoder's NaN -> signed maximum.
+__device__ __forceinline__ uint32_t e4m3x4_div(const float* x, float s, float r) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  float q[4];
+  bool slow = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[i] = x[i] * r;
+    const float aq = fabsf(q[i]);
+    const uint32_t key = (__float_as_uint(q[i]) & 0xFFFFFu) - (0x80000u - 4u);
+    slow |= key <= 8u || (aq < 0.015625f && aq != 0.0f) || !(aq == aq);
+  }
+  if (slow) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = x[i] / s;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = __builtin_copysignf(fminf(fabsf(q[i]), 448.0f), q[i]);
+  v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s){0, 0}, q[0], q[1], 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, q[2], q[3], 1.0f, true);
+  return __builtin_bit_cast(uint32_t, w);
+}
+
 // Value of a non-negative E4M3 byte (0x00..0x7E) as fp32, exactly.
 __device__ __forceinline__ float e4m3_value(uint32_t b) {
   const uint32_t e = (b >> 3) & 0xFu, m = b & 7u;

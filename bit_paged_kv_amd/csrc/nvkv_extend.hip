@@ -37,12 +37,10 @@ __global__ __launch_bounds__(256) void fp8_ws_append_kernel(const uint8_t* __res
   bf16x8_to_f32(src[0], x);
   bf16x8_to_f32(src[1], x + 8);
   const float s = is_v ? sv : sk;
+  const float r = 1.0f / s;
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w[i] = e4m3_encode(x[4 * i] / s) | (e4m3_encode(x[4 * i + 1] / s) << 8) |
-           (e4m3_encode(x[4 * i + 2] / s) << 16) | (e4m3_encode(x[4 * i + 3] / s) << 24);
-  }
+  for (int i = 0; i < 4; ++i) w[i] = e4m3x4_div(x + 4 * i, s, r);
   const size_t dst_row = (size_t)ws_offsets[b] + (size_t)prefix_lens[b] + tok;
   *reinterpret_cast<uint4*>((is_v ? v_ws : k_ws) + (dst_row * hkv * 128 + rest * 16)) =
       make_uint4(w[0], w[1], w[2], w[3]);

@@ -149,11 +149,10 @@ __global__ __launch_bounds__(kQThreads) void nvfp4_quantize_kernel(
     if constexpr (kWs) {
       if (tr < kQWin) {
         const float s = is_v ? sv_ws : sk_ws;
+        const float r = 1.0f / s;
         uint32_t w[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          w[i] = e4m3_encode(x[4 * i] / s) | (e4m3_encode(x[4 * i + 1] / s) << 8) |
-                 (e4m3_encode(x[4 * i + 2] / s) << 16) | (e4m3_encode(x[4 * i + 3] / s) << 24);
+        for (int i = 0; i < 4; ++i) w[i] = e4m3x4_div(x + 4 * i, s, r);
         *reinterpret_cast<uint4*>((is_v ? v_ws : k_ws) + ((size_t)t * hkv + h) * 128 + 16 * j) =
             make_uint4(w[0], w[1], w[2], w[3]);
       }
@@ -260,6 +259,7 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(
   const int t0 = (int)(gh / hkv) * 4;
   const int nt = min(4, n_tok - t0);
   const float s = is_v ? sv : sk;
+  const float r = 1.0f / s;
   const bool quad = is_v && aligned_quad(slots, t0, nt);
   uint32_t rows[16];
 #pragma unroll
@@ -270,7 +270,11 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(
     load_block16(is_v ? v_in : k_in, 0, 1.0f, (t * hkv + h) * 128 + 16 * j, x);
     uint32_t b[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) b[i] = e4m3_encode(x[i] / s);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = e4m3x4_div(x + 4 * i, s, r);
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) b[4 * i + k2] = (w >> (8 * k2)) & 0xFFu;
+    }
     const int slot = slots[t];
     const int o = slot & 15;
     const size_t blk = (size_t)(slot >> 4) * hkv + h;

@@ -207,6 +207,59 @@ def test_fp8_quantize_bitexact(nv):
     assert np.array_equal(pool["v"].cpu().numpy(), want_v)
 
 
+def _fp8_edge_values():
+    """Every E4M3 magnitude and every midpoint between neighbours (normal and subnormal), values at
+    and past the 448 saturation (up to inf), zeros, both signs: all exact in bf16."""
+    pos = o_codecs.E4M3_POSITIVE
+    mids = (pos[:-1] + pos[1:]) / 2
+    extra = np.array([448.0, 456.0, 464.0, 472.0, 480.0, 9984.0, np.inf, 0.0, 2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -11])
+    mags = np.concatenate([pos, mids, extra])
+    vals = np.concatenate([mags, -mags]).astype(np.float32)
+    bf = torch.from_numpy(vals).to(torch.bfloat16)
+    assert np.array_equal(bf.float().numpy(), vals)                 # all representable in bf16
+    return vals
+
+
+@pytest.mark.parametrize("s", [1.0, 1.0 + 2.0 ** -23, 1.0 - 2.0 ** -24, 1.0 + 3 * 2.0 ** -23, 1.0 - 3 * 2.0 ** -24,
+                               2.0 ** -3 * (1.0 + 2.0 ** -22), 0.75])
+def test_fp8_encode_near_rounding_midpoints_bitexact(nv, s):
+    """FP8 bytes of x / s where the quotients sit on, or a few fp32 ulps from, every E4M3 rounding
+    midpoint, in the saturation range and next to zero: the FP8 cache write, the workspace append
+    and the prefill copy all match the oracle byte for byte (RNE on the correctly rounded quotient)."""
+    vals = _fp8_edge_values()
+    s = float(np.float32(s))
+    reps = -(-vals.size // 256) * 256
+    x = np.resize(vals, reps).reshape(-1, 2, 128)                    # [tokens][2 heads][128]
+    x[:, 1] = x[:, 1][:, ::-1]                                       # head 1: another order
+    n_tok = x.shape[0]
+    want = o_fp8.fp8_quantize(x, s)
+    xb = torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+    # FP8 cache write
+    pages = -(-n_tok // 16)
+    slots = torch.arange(n_tok, dtype=torch.int32, device=DEV)
+    pool = nv.alloc_fp8_pool(pages, 2, DEV, fill=0x7F)
+    nv.fp8_quantize_append(xb, xb, slots, s, s, pool)
+    want_pool = np.full(o_layout.fp8_pool_shape(pages, 2), 0x7F, np.uint8)
+    o_layout.write_fp8_tokens(want_pool, "k", np.arange(n_tok), want)
+    assert np.array_equal(pool["k"].cpu().numpy(), want_pool)
+    # workspace append of a chunk (rows after a 3-row prefix)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    kw = torch.full((n_tok + 3, 2, 128), 0x7F, dtype=torch.uint8, device=DEV)
+    vw = kw.clone()
+    nv.fp8_workspace_append(xb, xb, t(np.array([0, n_tok], np.int32)), t(np.array([0], np.int32)),
+                            t(np.array([3], np.int32)), n_tok, 3, s, s, 2, kw, vw)
+    assert np.array_equal(kw.cpu().numpy()[3:], want)
+    assert np.array_equal(vw.cpu().numpy()[3:], want)
+    # prefill copy (written with the NVFP4 cache in one pass)
+    pool4 = nv.alloc_nvfp4_pool(pages, 2, DEV)
+    kc = torch.empty((n_tok, 2, 128), dtype=torch.uint8, device=DEV)
+    vc = torch.empty_like(kc)
+    nv.nvfp4_prefill_write(xb, xb, slots, 1.0, 1.0, pool4, s, s, kc, vc)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), want)
+    assert np.array_equal(vc.cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("case", ["small", "many-pages"])
 def test_dequant_to_workspace_bitexact(nv, case):
     if case == "small":
