@@ -87,8 +87,8 @@ EVENT_EVERY = 5     # decode configs: timed steps per dispatch-recorded kernel d
 # (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives (x2.000 / x1.000).  Valid only
 # for the kernel source and the split plan they were taken with; reported as null otherwise.
 TRAFFIC = {
-    "long": {"source_sha256": "6dcd6113121cfd45865aa21931858a7b8e8111b2882d0174adbeca859244a5e1",
-             "plan": [512, 16], "fetch_kib": 296024.8, "write_kib": 2203.9, "fetch_factor": 2.0,
+    "long": {"source_sha256": "a4106febd36095bbedeb9ff9291c30a2414ae4cca6a6f1bbe1c992b300954a5a",
+             "plan": [512, 16], "fetch_kib": 296025.4, "write_kib": 2210.2, "fetch_factor": 2.0,
              "write_factor": 1.0},
 }
 

@@ -243,6 +243,11 @@ __device__ __forceinline__ int opaque_lane_id() {
   return l;
 }
 
+// Splits that a sequence of n_pages pages uses under the plan (pages_per_split, num_splits).
+__device__ __forceinline__ int seq_splits(int n_pages, int pages_per_split, int num_splits) {
+  return min(num_splits, max(1, (n_pages + pages_per_split - 1) / pages_per_split));
+}
+
 // Workspace of a multi-split decode: per (row = b * Hq + h, split) the unnormalised partial output
 // [128] (times g_V), then per (row, split) its (max, sum) in log2 units.  Every entry is written
 // before it is read, so the workspace needs no initialisation.
@@ -265,9 +270,13 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
   const int group = a.hq / a.hkv;
   const int seq_len = a.seq_lens[b];
   const int n_pages = (seq_len + kPageSize - 1) / kPageSize;
-  // this workgroup's pages; the last split also takes any remainder
-  const int wg_begin = min(split * a.pages_per_split, n_pages);
-  const int wg_end = (split == a.num_splits - 1) ? n_pages : min(n_pages, wg_begin + a.pages_per_split);
+  // This sequence needs ceil(pages / pages_per_split) splits (at least one, at most num_splits),
+  // the last of them taking the remainder; the grid's other splits of the stream exit here and
+  // write nothing (the merge reads only the splits a sequence has).
+  const int n_split_b = seq_splits(n_pages, a.pages_per_split, a.num_splits);
+  if (split >= n_split_b) return;
+  const int wg_begin = split * a.pages_per_split;
+  const int wg_end = (split == n_split_b - 1) ? n_pages : wg_begin + a.pages_per_split;
   // each wave takes a contiguous, even-sized quarter of them
   const int quarter = (((wg_end - wg_begin + kWaves - 1) / kWaves) + 1) & ~1;
   const int pg_begin = min(wg_end, wg_begin + wave * quarter);
@@ -558,29 +567,47 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
   }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, query head) per block: 8 groups of 32 threads
-// each walk every 8th split with a running maximum (4 channels per thread), then the 8 group
-// states are combined through LDS.  Spreading the splits over lanes keeps the load chains short.
+// Log-sum-exp merge of the splits of one (sequence, query head) per block, over the splits that
+// sequence has (a short sequence of a ragged batch writes fewer than num_splits): 8 groups of 32
+// threads each walk every 8th split with a running maximum (4 channels per thread), then the 8
+// group states are combined through LDS.  Spreading the splits over lanes keeps the load chains
+// short.
 constexpr int kMergeGroups = 8;
 __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, int num_splits,
-                                                           float* __restrict__ out) {
+                                                           const int32_t* __restrict__ seq_lens, int hq,
+                                                           int pages_per_split, float* __restrict__ out) {
   const size_t row = blockIdx.x;
   const int g = threadIdx.x >> 5;
   const int d = (threadIdx.x & 31) * 4;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + row * num_splits;
   const float* po = part_o + row * num_splits * kHeadDim + d;
+  const int seq_len = seq_lens[row / (unsigned)hq];
+  // The first split of each group is read before the row's split count is known, at an index
+  // clamped into the row's num_splits entries; an entry past the count was not written by this
+  // launch and is dropped unused.
+  const int g0 = min(g, num_splits - 1);
+  float2 v = ml[g0];
+  f4 ov = *reinterpret_cast<const f4*>(po + (size_t)g0 * kHeadDim);
+  // all three reads in flight together (the compiler would otherwise sink the partials' reads
+  // below the split count they do not depend on)
+  asm volatile("" ::"s"(seq_len), "v"(v.x), "v"(v.y), "v"(ov[0]), "v"(ov[1]), "v"(ov[2]), "v"(ov[3]));
+  const int n_split_b = seq_splits((seq_len + kPageSize - 1) / kPageSize, pages_per_split, num_splits);
   float m = -INFINITY, den = 0.0f;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = g; s < num_splits; s += kMergeGroups) {
-    const float2 v = ml[s];
-    const f4 ov = *reinterpret_cast<const f4*>(po + (size_t)s * kHeadDim);
-    if (v.y > 0.0f) {   // empty splits carry no partial output
-      const float m_new = fmaxf(m, v.x);
+  for (int s = g; s < n_split_b; s += kMergeGroups) {
+    const float2 vc = v;
+    const f4 oc = ov;
+    if (s + kMergeGroups < n_split_b) {   // the group's next split, read before this one's arithmetic
+      v = ml[s + kMergeGroups];
+      ov = *reinterpret_cast<const f4*>(po + (size_t)(s + kMergeGroups) * kHeadDim);
+    }
+    if (vc.y > 0.0f) {   // empty splits carry no partial output
+      const float m_new = fmaxf(m, vc.x);
       const float f_old = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
-      const float f_new = __builtin_amdgcn_exp2f(v.x - m_new);
-      den = den * f_old + v.y * f_new;
-      acc = acc * f_old + ov * f_new;
+      const float f_new = __builtin_amdgcn_exp2f(vc.x - m_new);
+      den = den * f_old + vc.y * f_new;
+      acc = acc * f_old + oc * f_new;
       m = m_new;
     }
   }
@@ -636,7 +663,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t sta
   const float* part_o = reinterpret_cast<const float*>(a.workspace);
   const float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
   hipLaunchKernelGGL(merge_splits_kernel, dim3(a.batch * a.hq), dim3(256), 0, stream, part_o, part_ml, a.num_splits,
-                     a.out);
+                     a.seq_lens, a.hq, a.pages_per_split, a.out);
   return hipGetLastError();
 }
 

@@ -119,10 +119,11 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
                            uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream);
 
 /*
- * Split planning for decode.  The sequence axis is cut into splits of `pages_per_split` pages;
- * each (sequence, kv head, split) is one workgroup of four wavefronts (each takes a contiguous
- * quarter of the split and the four combine in LDS); with several splits a second kernel merges the
- * partial softmax states.
+ * Split planning for decode.  A sequence of P pages is cut into n = min(num_splits,
+ * ceil(P / pages_per_split)) splits (at least one) of pages_per_split pages, the last taking the
+ * remainder; each (sequence, kv head, split < n) is one workgroup of four wavefronts (each takes a
+ * contiguous quarter of the split and the four combine in LDS), the grid's workgroups for splits
+ * >= n exit at once, and with several splits a second kernel merges the n partial softmax states.
  * nvkv_plan_decode picks num_splits from host-side hints so that the grid fills the GPU (exactly
  * two workgroups per compute unit when the lengths are equal and the stream count batch *
  * num_kv_heads allows it, else about three, or 4.5 for a ragged batch):
@@ -131,7 +132,7 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
  *   force_pages_per_split : > 0 forces the split size (rounded up to even); 0 = automatic.
  * Outputs *pages_per_split (even, >= 2) and *num_splits (>= 1) with
  * num_splits * pages_per_split * 16 >= max_seq_len.  A sequence longer than that still runs
- * correctly: the last split takes the remainder.
+ * correctly: its last split takes all the remaining pages.
  */
 NVKV_API int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long total_tokens,
                      int force_pages_per_split, int* pages_per_split, int* num_splits);

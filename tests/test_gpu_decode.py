@@ -67,6 +67,17 @@ def test_decode_split_count_invariance(nv, ragged):
         assert np.abs(o - outs[0]).max() < 1e-5
 
 
+@pytest.mark.parametrize("plan", [(2, 3), (3, 2), (5, 1), (7, 4)])
+def test_decode_plan_shorter_than_sequences(nv, ragged, plan):
+    """Plans whose num_splits x pages_per_split pages do not cover the longest sequences: each
+    sequence's splits grow to hold all of its pages."""
+    wl, pool, gk, gv, want = ragged
+    pt, sl = H.gpu_tables(wl, DEV)
+    got = nv.nvfp4_decode(wl.q().to(DEV), pool, float(gk), float(gv), pt, sl, wl.sm_scale, plan, wl.h_kv)
+    torch.cuda.synchronize()
+    H.assert_attention_close(got.cpu().numpy(), want, f"plan {plan}")
+
+
 @pytest.mark.parametrize("group", [1, 2, 8, 16])
 def test_decode_gqa_groups(nv, group):
     wl = workloads.Workload(name=f"gqa{group}", seed=30 + group, batch=2, h_kv=2, h_q=2 * group,
