@@ -87,8 +87,8 @@ EVENT_EVERY = 5     # decode configs: timed steps per dispatch-recorded kernel d
 # (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives (x2.000 / x1.000).  Valid only
 # for the kernel source and the split plan they were taken with; reported as null otherwise.
 TRAFFIC = {
-    "long": {"source_sha256": "a4106febd36095bbedeb9ff9291c30a2414ae4cca6a6f1bbe1c992b300954a5a",
-             "plan": [512, 16], "fetch_kib": 296025.4, "write_kib": 2210.2, "fetch_factor": 2.0,
+    "long": {"source_sha256": "a5e48bdd8a38d9f3835cf10471306e35b5190d548fa07d568d0dfae52fcbcaeb",
+             "plan": [512, 16], "fetch_kib": 296024.1, "write_kib": 2209.2, "fetch_factor": 2.0,
              "write_factor": 1.0},
 }
 

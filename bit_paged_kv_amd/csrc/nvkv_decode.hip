@@ -311,35 +311,43 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
   for (int n = 0; n < 8; ++n) o[n] = f4{0.f, 0.f, 0.f, 0.f};
 
   if (pg_begin < pg_end) {
-    // q row -> fp16 B operands, rescaled by a power of two so the row maximum sits in [2^13, 2^14)
-    float qf[32];
-    if (head_ok) {
+    // q row -> fp16 B operands, rescaled by a power of two so the row maximum sits in [2^13, 2^14).
+    // The raw row is loaded with the first page ids (every lane reads a valid row: absent heads
+    // read head 0 and zero it), and converted while the first pages are in flight, so the wave
+    // waits for two memory round trips before its first scores, not three.
+    h8 qb[4];
+    float qk_scale = 0.0f;
+    uint4 q_raw[4];
+    auto load_q = [&] {
       const uint4* qp =
           reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + row * kHeadDim + 32 * c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bf16x8_to_f32(qp[i], qf + 8 * i);
-    } else {
+      for (int i = 0; i < 4; ++i) q_raw[i] = qp[i];
+    };
+    auto prep_q = [&] {
+      float qf[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) qf[i] = 0.0f;
-    }
-    float qmax = 0.0f;
+      for (int i = 0; i < 4; ++i) bf16x8_to_f32(q_raw[i], qf + 8 * i);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qf[i]));
-    qmax = max_xor16(qmax);
-    qmax = max_xor32(qmax);
-    int qexp = 0;
-    if (qmax > 0.0f) {
-      int ex;
-      (void)frexpf(qmax, &ex);          // qmax = f * 2^ex, f in [0.5, 1)
-      qexp = min(max(14 - ex, -100), 100);
-    }
-    h8 qb[4];
+      for (int i = 0; i < 32; ++i) qf[i] = head_ok ? qf[i] : 0.0f;
+      float qmax = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qf[i]));
+      qmax = max_xor16(qmax);
+      qmax = max_xor32(qmax);
+      int qexp = 0;
+      if (qmax > 0.0f) {
+        int ex;
+        (void)frexpf(qmax, &ex);          // qmax = f * 2^ex, f in [0.5, 1)
+        qexp = min(max(14 - ex, -100), 100);
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qb[s][i] = (_Float16)__builtin_ldexpf(qf[8 * s + i], qexp);
-    // scores in log2 units: <q, K_hat> * sm_scale * log2(e); K_hat = (e2m1 * s_blk) * g_K
-    const float qk_scale = a.sm_scale * 1.44269504088896341f * a.k_gscale * __builtin_ldexpf(1.0f, -qexp);
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qb[s][i] = (_Float16)__builtin_ldexpf(qf[8 * s + i], qexp);
+      // scores in log2 units: <q, K_hat> * sm_scale * log2(e); K_hat = (e2m1 * s_blk) * g_K
+      qk_scale = a.sm_scale * 1.44269504088896341f * a.k_gscale * __builtin_ldexpf(1.0f, -qexp);
+    };
     float thr = -INFINITY;    // raw score above which the running maximum must be raised
 
     // Every load below is unconditional: a pair index past the end is clamped to the last pair (a
@@ -464,8 +472,10 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
       load_ids(0, a0, a1);
       load_ids(1, b0, b1);
       load_ids(2, c0, c1);
+      load_q();
       issue(pa0, pa1, a0, a1);
       issue(pb0, pb1, b0, b1);
+      prep_q();
       scores(pa0, pa1, 0, npairs <= 1, x);
       for (int pr = 0;; pr += 3) {
         load_ids(pr + 3, a0, a1);
@@ -490,7 +500,9 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
       int a0, a1, b0, b1;
       load_ids(0, a0, a1);
       load_ids(1, b0, b1);
+      load_q();
       issue(pa0, pa1, a0, a1);
+      prep_q();
       scores(pa0, pa1, 0, npairs <= 1, x);
       for (int pr = 0;; pr += 2) {
         load_ids(pr + 2, a0, a1);
