@@ -21,7 +21,10 @@ duration comes from HIP events that its dispatch records on every 5th timed step
 dispatch adds a few microseconds to its step); extend and prefill time each attention launch with
 events on the launch stream.  Effective KV GB/s =
 NVFP4 (or FP8) bytes the step must read (144 B per token and KV head; 256 B for FP8) / step time.
-The CPU baseline times the fp64 oracle (dequantize + attention, one thread) on a bounded sample.
+The CPU baseline times the fp64 oracle (one thread per worker) on a bounded sample of the same
+workload: dequantize + attention for the decode configs and the mixed stack (each layer in its
+precision), the whole per-(layer, kv head) pipeline for extend, and for prefill the prompt's write
+plus a block of query rows whose attention time is scaled to the whole prompt by its flop ratio.
 """
 from __future__ import annotations
 
@@ -200,6 +203,179 @@ def cpu_baseline(cfg_index, budget_s=6.0):
                       f"(fp64 dequantize + softmax attention for {wl.group} query heads each), {spent:.1f} s of oracle "
                       f"time over {cores} single-threaded workers; rate summed over workers; host "
                       f"{platform.processor() or platform.machine()}"}
+
+
+def _cpu_mixed_units(args):
+    """One pool worker, 28-layer stack: the oracle's decode of (layer, sequence) units over all kv
+    heads, each layer in its own precision (NVFP4: dequantize blocks; FP8: dequantize E4M3 x s);
+    returns (KV bytes, seconds spent in the oracle)."""
+    cfg_index, units, budget_s = args
+    from threadpoolctl import threadpool_limits
+
+    import workloads
+    from oracle import attention as o_att
+    from oracle import fp8 as o_fp8
+    from oracle import nvfp4 as o_nv
+    wl = workloads.config(cfg_index)
+    g = wl.group
+    qs = {}
+    done_bytes, spent = 0, 0.0
+    with threadpool_limits(limits=1):
+        for layer, b in units:
+            if layer not in qs:
+                qs[layer] = wl.q(layer).float().numpy()
+            q = qs[layer][b]
+            k = wl.kv("k", b, layer).float().numpy()
+            v = wl.kv("v", b, layer).float().numpy()
+            fp8 = wl.is_fp8(layer)
+            if fp8:                                   # cache contents (not timed); scales of this sequence
+                sk, sv = o_fp8.fp8_scale(k), o_fp8.fp8_scale(v)
+                ck, cv = o_fp8.fp8_quantize(k, sk), o_fp8.fp8_quantize(v, sv)
+            else:
+                gk, gv = o_nv.global_scale(k), o_nv.global_scale(v)
+            for hk in range(wl.h_kv):
+                if not fp8:
+                    nk, nsk = o_nv.quantize_blocks(k[:, hk], gk)
+                    nvv, nsv = o_nv.quantize_blocks(v[:, hk], gv)
+                t0 = time.perf_counter()
+                if fp8:
+                    kh = o_fp8.fp8_dequantize(ck[:, hk], sk)[:, None]
+                    vh = o_fp8.fp8_dequantize(cv[:, hk], sv)[:, None]
+                else:
+                    kh = o_nv.dequantize_blocks(nk, nsk, gk)[:, None]
+                    vh = o_nv.dequantize_blocks(nvv, nsv, gv)[:, None]
+                o_att.decode_attention_one(q[hk * g:(hk + 1) * g], kh, vh, wl.sm_scale)
+                spent += time.perf_counter() - t0
+                done_bytes += k.shape[0] * (256 if fp8 else 144)
+                if spent >= budget_s:
+                    return done_bytes, spent
+    return done_bytes, spent
+
+
+def _cpu_extend_units(args):
+    """One pool worker, extend or prefill of the stack's NVFP4 layers: the oracle's pipeline for
+    (layer, kv head) units with the head's query group; returns (step bytes, seconds of oracle time
+    for the whole unit, attention flops of the whole unit, seconds measured).
+
+    extend: NVFP4 prefix -> FP8 workspace, chunk -> FP8 rows after it, causal attention of the
+    2048-row chunk over prefix || chunk, chunk -> NVFP4; all timed.
+    prefill: the prompt -> NVFP4 and the FP8 copy (timed), then causal attention of a block of
+    `rows` query rows whose mean visible-key count equals the prompt's (timed); the whole prompt's
+    attention time is that block's time scaled by the flop ratio."""
+    cfg_index, mode, units, budget_s, rows = args
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import workloads
+    from oracle import attention as o_att
+    from oracle import fp8 as o_fp8
+    from oracle import nvfp4 as o_nv
+    wl = workloads.config(cfg_index)
+    g = wl.group
+    prefix, chunk = wl.extend_prefix, wl.extend_chunk
+    if mode == "extend":
+        ext = workloads.Workload(name="extend", seed=wl.seed, batch=1, h_kv=wl.h_kv, h_q=wl.h_q,
+                                 seq_lens=[prefix + chunk], chan=wl.chan)
+        gen = torch.Generator().manual_seed(wl.seed * 7 + 5)
+        q_all = torch.randn((chunk, wl.h_q, 128), generator=gen).to(torch.bfloat16).float().numpy()
+    else:
+        ext = workloads.Workload(name="prefill", seed=wl.seed, batch=1, h_kv=wl.h_kv, h_q=wl.h_q,
+                                 seq_lens=[prefix], chan=wl.chan)
+        gen = torch.Generator().manual_seed(wl.seed * 7 + 6)
+        q_all = torch.randn((prefix, wl.h_q, 128), generator=gen).to(torch.bfloat16).float().numpy()
+    done_bytes, est, flops, spent = 0, 0.0, 0, 0.0
+    cur = None
+    with threadpool_limits(limits=1):
+        for layer, hk in units:
+            if cur is None or cur[0] != layer:
+                k = ext.kv("k", 0, layer, length=prefix).float().numpy()
+                v = ext.kv("v", 0, layer, length=prefix).float().numpy()
+                cur = (layer, k, v, o_nv.global_scale(k), o_nv.global_scale(v))
+            _, k, v, gk, gv = cur
+            s_wk, s_wv = np.float32(6.0 * gk), np.float32(6.0 * gv)
+            qg = q_all[:, hk * g:(hk + 1) * g]
+            if mode == "extend":
+                ck = wl.chunk("k", layer).float().numpy()[:, hk]
+                cv = wl.chunk("v", layer).float().numpy()[:, hk]
+                pk, psk = o_nv.quantize_blocks(k[:, hk], gk)          # the cached prefix (not timed)
+                pv, psv = o_nv.quantize_blocks(v[:, hk], gv)
+                t0 = time.perf_counter()
+                wk = np.concatenate([o_fp8.nvfp4_to_fp8_workspace(pk, psk, gk, s_wk), o_fp8.fp8_quantize(ck, s_wk)])
+                wv = np.concatenate([o_fp8.nvfp4_to_fp8_workspace(pv, psv, gv, s_wv), o_fp8.fp8_quantize(cv, s_wv)])
+                o_att.extend_attention_one(qg, o_fp8.fp8_dequantize(wk, s_wk)[:, None],
+                                           o_fp8.fp8_dequantize(wv, s_wv)[:, None], prefix, wl.sm_scale)
+                o_nv.quantize_blocks(ck, gk)
+                o_nv.quantize_blocks(cv, gv)
+                dt = time.perf_counter() - t0
+                spent += dt
+                est += dt
+                done_bytes += prefix * (144 + 256) + chunk * (512 + 144)
+                flops += 4 * 128 * g * (chunk * prefix + chunk * (chunk + 1) // 2)
+            else:
+                n = prefix
+                t0 = time.perf_counter()
+                o_nv.quantize_blocks(k[:, hk], gk)
+                o_nv.quantize_blocks(v[:, hk], gv)
+                wk, wv = o_fp8.fp8_quantize(k[:, hk], s_wk), o_fp8.fp8_quantize(v[:, hk], s_wv)
+                t1 = time.perf_counter()
+                r0 = (n - rows) // 2
+                o_att.extend_attention_one(qg[r0:r0 + rows], o_fp8.fp8_dequantize(wk[:r0 + rows], s_wk)[:, None],
+                                           o_fp8.fp8_dequantize(wv[:r0 + rows], s_wv)[:, None], r0, wl.sm_scale)
+                t2 = time.perf_counter()
+                full = n * (n + 1) // 2
+                sample = rows * r0 + rows * (rows + 1) // 2
+                spent += t2 - t0
+                est += (t1 - t0) + (t2 - t1) * full / sample
+                done_bytes += n * (512 + 144 + 256)
+                flops += 4 * 128 * g * full
+            if spent >= budget_s:
+                break
+    return done_bytes, est, flops, spent
+
+
+def cpu_baseline_stack(cfg_index, mode, budget_s=6.0, rows=1024):
+    """The oracle timed on the mixed stack (mode "mixed", KV GB/s) or on the extend / prefill step of
+    its NVFP4 layers (step GB/s, plus the oracle's attention TFLOP/s), one unit list per host core
+    (at most 16 spawned workers, each stopping after ~budget_s of oracle time)."""
+    import multiprocessing as mp
+
+    import workloads
+    wl = workloads.config(cfg_index)
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    if mode == "mixed":
+        all_units = [(layer, b) for b in range(wl.batch) for layer in range(wl.layers)]
+    else:
+        all_units = [(layer, hk) for layer in range(wl.layers) if not wl.is_fp8(layer) for hk in range(wl.h_kv)]
+    jobs = []
+    n = len(all_units)
+    for w in range(cores):
+        mine = all_units[w * n // cores:(w + 1) * n // cores]
+        jobs.append((cfg_index, mine, budget_s) if mode == "mixed" else (cfg_index, mode, mine, budget_s, rows))
+    with mp.get_context("spawn").Pool(cores) as pool:
+        res = pool.map(_cpu_mixed_units if mode == "mixed" else _cpu_extend_units, jobs)
+    host = platform.processor() or platform.machine()
+    if mode == "mixed":
+        total = sum(r[0] for r in res)
+        rate = sum(r[0] / r[1] for r in res if r[1] > 0)
+        spent = sum(r[1] for r in res)
+        return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"{total} KV bytes of (layer, sequence) units taken in layer order per sequence (each "
+                          f"layer in its own precision, FP8 scales of the unit's sequence; fp64 dequantize + "
+                          f"softmax attention over 8 kv heads), {spent:.1f} s of oracle time over {cores} "
+                          f"single-threaded workers; rate summed over workers; host {host}"}
+    total = sum(r[0] for r in res)
+    rate = sum(r[0] / r[1] for r in res if r[1] > 0)
+    tflops = sum(r[2] / r[1] for r in res if r[1] > 0) / 1e12
+    spent = sum(r[3] for r in res)
+    what = ("the whole per-(layer, kv head) pipeline: prefix gather to FP8, chunk append, causal attention of "
+            "2048 chunk rows x 4 query heads over 18432 keys, chunk quantize-append" if mode == "extend" else
+            f"the prompt's NVFP4 + FP8 write, then causal attention of {rows} query rows x 4 query heads whose "
+            f"mean key count is the prompt's, the whole prompt's attention time taken as that block's time x the "
+            f"flop ratio")
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "attention_tflops": round(tflops, 6),
+            "sample": f"{total} step bytes of (layer, kv head) units ({what}; fp64), {spent:.1f} s of oracle "
+                      f"time over {cores} single-threaded workers; rate summed over workers; host {host}"}
 
 
 # ------------------------------------------------------------------------------------------------
@@ -515,6 +691,12 @@ def main():
     if not args.no_cpu_baseline and name in ("long", "batch32", "ragged", "tiny"):
         cpu = cpu_baseline(index)
         log(f"cpu baseline {cpu['value']} GB/s")
+    elif not args.no_cpu_baseline and name in ("mixed", "extend", "prefill"):
+        # mixed: the untimed cache preparation (quantizing each unit's K/V) takes ~25x the timed decode,
+        # so its workers stop after 1 s of oracle time to keep the run within a minute
+        cpu = cpu_baseline_stack(index, name, budget_s=1.0 if name == "mixed" else 6.0)
+        log(f"cpu baseline {cpu['value']} GB/s" +
+            (f", attention {cpu['attention_tflops']} TFLOP/s" if "attention_tflops" in cpu else ""))
 
     traffic, traffic_detail = None, None
     t = TRAFFIC.get(name)
