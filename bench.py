@@ -413,8 +413,8 @@ def precision_studies(nv, workloads, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part of "
-                                   "this build (see the sharding notes in DESIGN.md)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the library has no multi-GPU path, "
+                                   "so --gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
 
