@@ -257,6 +257,68 @@ def test_full_size_ragged_fused_sampled(nv):
     _sampled_full_size(nv, 3, [(longest, 2), (shortest, 5)])
 
 
+@pytest.mark.timeout(900)
+def test_full_size_mixed_stack_sampled(nv):
+    """The 28-layer stack's shape (44 x 8192 tokens, 8 KV / 32 query heads) in the bench's plan, one
+    FP8 layer and one NVFP4 layer dispatched together by nvkv_decode_layers; sampled (sequence, kv
+    head) rows against the oracle, which derives every scale from the seeded inputs itself."""
+    from bit_paged_kv_amd import paged
+    wl = workloads.config(4)
+    fp8_layer = int(wl.fp8_layers[0])
+    nv4_layer = next(l for l in range(wl.layers) if not wl.is_fp8(l))
+    pt, sl = H.gpu_tables(wl, DEV)
+    plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), int(wl.total_lens.sum()))
+    slots = torch.from_numpy(np.concatenate([wl.slots(b) for b in range(wl.batch)])).to(DEV)
+    layers, host = [], {}
+    for layer in (fp8_layer, nv4_layer):
+        ks = [wl.kv("k", b, layer) for b in range(wl.batch)]
+        vs = [wl.kv("v", b, layer) for b in range(wl.batch)]
+        k_all, v_all = torch.cat(ks).to(DEV), torch.cat(vs).to(DEV)
+        if wl.is_fp8(layer):
+            pool, s1, s2 = paged.build_fp8_cache(k_all, v_all, slots, wl.num_pages)
+            prec = nv.PREC_FP8
+        else:
+            pool, s1, s2 = paged.build_nvfp4_cache(k_all, v_all, slots, wl.num_pages)
+            prec = nv.PREC_NVFP4
+        del k_all, v_all
+        layers.append(dict(precision=prec, q=wl.q(layer).to(DEV), pool=pool, k_gscale=s1, v_gscale=s2,
+                           out=torch.empty((wl.batch, wl.h_q, 128), dtype=torch.float32, device=DEV)))
+        amax_k = np.array([max(float(t.float().abs().max()) for t in ks)], np.float32)
+        amax_v = np.array([max(float(t.float().abs().max()) for t in vs)], np.float32)
+        host[layer] = (ks, vs, amax_k, amax_v, s1, s2)
+        print(f"mixed full size: layer {layer} cache built", flush=True)
+    outs = [o.cpu().numpy() for o in nv.decode_layers(layers, pt, sl, wl.sm_scale, plan, wl.h_kv)]
+    print(f"mixed full size: GPU step done, plan {plan}", flush=True)
+    del layers
+    torch.cuda.empty_cache()
+    G = wl.group
+    for i, layer in enumerate((fp8_layer, nv4_layer)):
+        ks, vs, amax_k, amax_v, s1, s2 = host[layer]
+        qf = wl.q(layer).float().numpy()
+        fp8 = wl.is_fp8(layer)
+        if fp8:
+            ok, ov = o_fp8.fp8_scale(amax_k), o_fp8.fp8_scale(amax_v)
+        else:
+            ok, ov = o_nv.global_scale(amax_k), o_nv.global_scale(amax_v)
+        assert (np.float32(s1), np.float32(s2)) == (ok, ov), f"layer {layer} scales"
+        for b, hk in [(0, 0), (21, 5), (43, 7)]:
+            k = ks[b][:, hk].float().numpy()
+            v = vs[b][:, hk].float().numpy()
+            if fp8:
+                kh = o_fp8.fp8_dequantize(o_fp8.fp8_quantize(k, ok), ok)[:, None]
+                vh = o_fp8.fp8_dequantize(o_fp8.fp8_quantize(v, ov), ov)[:, None]
+            else:
+                ck, sk = o_nv.quantize_blocks(k, ok)
+                cv, sv = o_nv.quantize_blocks(v, ov)
+                kh = o_nv.dequantize_blocks(ck, sk, ok)[:, None]
+                vh = o_nv.dequantize_blocks(cv, sv, ov)[:, None]
+            want = o_att.decode_attention_one(qf[b, hk * G:(hk + 1) * G], kh, vh, wl.sm_scale)
+            err = H.assert_attention_close(outs[i][b, hk * G:(hk + 1) * G], want,
+                                           f"mixed layer {layer} b={b} hk={hk} plan={plan}")
+            print(f"mixed full size: layer {layer} b={b} hk={hk} max-abs {err[0]:.2e} rel-L2 {err[1]:.2e}",
+                  flush=True)
+
+
 def test_workspace_reused_across_plans(nv, ragged):
     wl, pool, gk, gv, want = ragged
     pt, sl = H.gpu_tables(wl, DEV)

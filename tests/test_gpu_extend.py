@@ -287,3 +287,60 @@ def test_prefill_write_and_attention(nv, lens):
                              float(s_wk), float(s_wv), wl.sm_scale, wl.h_kv, max(lens), 0)
     torch.cuda.synchronize()
     H.assert_attention_close(out.cpu().numpy(), want, f"prefill {lens}")
+
+
+@pytest.mark.timeout(900)
+def test_prefill_full_size_sampled(nv):
+    """The bench's prefill workload at full size (one 16384-token prompt of an NVFP4 layer, 8 KV /
+    32 query heads) through the bench's calls: the one-pass write's NVFP4 pool and FP8 copy are
+    byte-exact against the oracle's quantizers, and sampled query rows (all heads) of the causal
+    attention over the copy match the oracle's attention over the keys they see."""
+    wl = workloads.config(4)
+    layer = 1
+    assert not wl.is_fp8(layer)
+    n = wl.extend_prefix
+    ext = workloads.Workload(name="prefill", seed=wl.seed, batch=1, h_kv=wl.h_kv, h_q=wl.h_q, seq_lens=[n],
+                             chan=wl.chan)
+    k = ext.kv("k", 0, layer)
+    v = ext.kv("v", 0, layer)
+    rng = np.random.default_rng(2025)
+    q = _bf16(rng.standard_normal((n, wl.h_q, 128)))
+    print("prefill full size: inputs generated", flush=True)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    slots = ext.slots(0, 0, n)
+    kd, vd = k.to(DEV), v.to(DEV)
+    gk = float(nv.global_scale(kd).item())
+    gv = float(nv.global_scale(vd).item())
+    s_wk, s_wv = 6.0 * gk, 6.0 * gv
+    pool = nv.alloc_nvfp4_pool(ext.num_pages, wl.h_kv, DEV)
+    kw = torch.empty((n, wl.h_kv, 128), dtype=torch.uint8, device=DEV)
+    vw = torch.empty_like(kw)
+    nv.nvfp4_prefill_write(kd, vd, t(slots), gk, gv, pool, s_wk, s_wv, kw, vw)
+    offs = torch.tensor([0, n], dtype=torch.int32, device=DEV)
+    zero = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = nv.fp8_extend_attn(q.to(DEV), offs, kw, vw, offs, zero, s_wk, s_wv, wl.sm_scale, wl.h_kv, n, 0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    got_kw, got_vw = kw.cpu().numpy(), vw.cpu().numpy()
+    got_pool = H.pool_to_numpy(pool)
+    print("prefill full size: GPU done", flush=True)
+    kn, vn = k.float().numpy(), v.float().numpy()
+    g_k, g_v = o_nv.global_scale(kn), o_nv.global_scale(vn)
+    assert (np.float32(gk), np.float32(gv)) == (g_k, g_v)
+    sw_k, sw_v = np.float32(6.0) * g_k, np.float32(6.0) * g_v
+    # the FP8 copy, every byte
+    want_kw, want_vw = o_fp8.fp8_quantize(kn, sw_k), o_fp8.fp8_quantize(vn, sw_v)
+    assert np.array_equal(got_kw, want_kw)
+    assert np.array_equal(got_vw, want_vw)
+    # the NVFP4 pool, every byte of the prompt's pages
+    want_pool = H.oracle_nvfp4_pool(ext, [kn], [vn], g_k, g_v)
+    for key in ("k_data", "k_scale", "v_data", "v_scale"):
+        assert np.array_equal(got_pool[key], want_pool[key]), key
+    print("prefill full size: write bytes exact", flush=True)
+    k_hat = o_fp8.fp8_dequantize(want_kw, sw_k)
+    v_hat = o_fp8.fp8_dequantize(want_vw, sw_v)
+    qn = q.float().numpy()
+    rows = [0, 1, 63, 64, 4095, 8191, 16382, 16383] + list(rng.integers(0, n, 8))
+    want = np.stack([o_att.decode_attention_one(qn[i], k_hat[:i + 1], v_hat[:i + 1], wl.sm_scale) for i in rows])
+    err = H.assert_attention_close(got[rows], want, "prefill full size, sampled rows")
+    print(f"prefill full size: sampled rows max-abs {err[0]:.2e} rel-L2 {err[1]:.2e}", flush=True)
