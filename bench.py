@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark: NVFP4 paged decode attention on one MI355X -- effective KV GB/s (% of HBM peak) + tokens/s.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long|batch32|ragged|mixed|extend|prefill|tiny|sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--config long|batch32|ragged|mixed|extend|prefill|write|tiny|sweep]
 
 One step is one decode step of the workload's hot path, inputs already resident in HBM:
   long     split-K NVFP4 decode + log-sum-exp merge, 4 x 131072 tokens, 8 KV / 64 query heads (default)
@@ -13,6 +14,8 @@ One step is one decode step of the workload's hot path, inputs already resident 
            chunk quantize-append (24 layers per step)
   prefill  per NVFP4 layer: one-pass NVFP4 cache + FP8 copy write of a prompt and causal attention
            over the copy
+  write    quantize-on-write of the ragged batch's whole cache (495,439 tokens x 8 kv heads, bf16 K
+           and V) into a fresh NVFP4 pool; the per-tensor scale reduction is timed apart
   tiny     1 x 256 tokens (latency-bound)
   sweep    precision studies (per-layer NVFP4 vs FP8 sensitivity, per-tensor scale variants)
 
@@ -47,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="long", choices=["long", "batch32", "ragged", "mixed", "extend", "prefill",
-                                                         "tiny", "sweep"])
+                                                         "write", "tiny", "sweep"])
     ap.add_argument("--pages-per-split", type=int, default=0, help="force the split size (0 = planner)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -88,19 +91,26 @@ EVENT_EVERY = 5     # decode configs: timed steps per dispatch-recorded kernel d
 
 # HBM traffic of decode_split_kernel on the long workload, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives (x2.000 / x1.000).  Valid only
-# for the kernel source and the split plan they were taken with; reported as null otherwise.
+# for the kernel sources (the decode file and the headers it includes, hashed together) and the
+# split plan they were taken with; reported as null otherwise.
 TRAFFIC = {
-    "long": {"source_sha256": "a5e48bdd8a38d9f3835cf10471306e35b5190d548fa07d568d0dfae52fcbcaeb",
-             "plan": [512, 16], "fetch_kib": 296024.1, "write_kib": 2209.2, "fetch_factor": 2.0,
+    "long": {"source_sha256": "f69eb3d6530819662c03d1604cb0db9a00ef6e95cc9bffe2b8be9d511e19b638",
+             "plan": [512, 16], "fetch_kib": 296023.6, "write_kib": 2208.1, "fetch_factor": 2.0,
              "write_factor": 1.0},
 }
 
 
+DECODE_SOURCES = ("nvkv_decode.hip", "nvkv_device.h", "nvkv_launch.h")
+
+
 def decode_source_sha256():
+    """sha256 over the decode kernel's sources, concatenated in DECODE_SOURCES order."""
     import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_paged_kv_amd", "csrc", "nvkv_decode.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_paged_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def stream_read_ceiling(nv, nbytes, dev, reps=20):
@@ -333,6 +343,60 @@ def _cpu_extend_units(args):
     return done_bytes, est, flops, spent
 
 
+def _cpu_write_units(args):
+    """One pool worker, quantize-on-write: the oracle's NVFP4 block quantizer (fp32, one thread) on
+    (sequence, kv head) units' K and V; returns (bytes as the kernel counts them, seconds)."""
+    cfg_index, units, budget_s = args
+    from threadpoolctl import threadpool_limits
+
+    import workloads
+    from oracle import nvfp4 as o_nv
+    wl = workloads.config(cfg_index)
+    done_bytes, spent = 0, 0.0
+    with threadpool_limits(limits=1):
+        for b, hks in units:
+            k = wl.kv("k", b).float().numpy()
+            v = wl.kv("v", b).float().numpy()
+            gk, gv = o_nv.global_scale(k), o_nv.global_scale(v)      # this sequence's scales (not timed)
+            for hk in hks:
+                t0 = time.perf_counter()
+                o_nv.quantize_blocks(k[:, hk], gk)
+                o_nv.quantize_blocks(v[:, hk], gv)
+                spent += time.perf_counter() - t0
+                done_bytes += k.shape[0] * (512 + 144)
+                if spent >= budget_s:
+                    return done_bytes, spent
+    return done_bytes, spent
+
+
+def cpu_baseline_write(cfg_index, budget_s=6.0):
+    """The oracle's quantizer timed on (sequence, kv head) units of the workload's cache, one unit list
+    per host core (at most 16 spawned workers, ~budget_s of oracle time each); summed GB/s."""
+    import multiprocessing as mp
+
+    import workloads
+    wl = workloads.config(cfg_index)
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    # units spread over the batch so that every worker sees long and short sequences
+    all_units = [(b, hk) for hk in range(wl.h_kv) for b in range(wl.batch)]
+    jobs = []
+    for w in range(cores):
+        by_seq = {}
+        for b, hk in all_units[w::cores]:
+            by_seq.setdefault(b, []).append(hk)
+        jobs.append((cfg_index, sorted(by_seq.items()), budget_s))
+    with mp.get_context("spawn").Pool(cores) as pool:
+        res = pool.map(_cpu_write_units, jobs)
+    total = sum(r[0] for r in res)
+    rate = sum(r[0] / r[1] for r in res if r[1] > 0)
+    spent = sum(r[1] for r in res)
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{total} bytes (bf16 K+V read, NVFP4 written) of (sequence, kv head) units of the ragged "
+                      f"cache (fp32 NVFP4 block quantizer of K and V; scales of the unit's sequence), {spent:.1f} s of "
+                      f"oracle time over {cores} single-threaded workers; rate summed over workers; host "
+                      f"{platform.processor() or platform.machine()}"}
+
+
 def cpu_baseline_stack(cfg_index, mode, budget_s=6.0, rows=1024):
     """The oracle timed on the mixed stack (mode "mixed", KV GB/s) or on the extend / prefill step of
     its NVFP4 layers (step GB/s, plus the oracle's attention TFLOP/s), one unit list per host core
@@ -430,7 +494,7 @@ def main():
     if name == "sweep":
         precision_studies(nv, workloads, dev)
         return
-    index = {"tiny": 0, "batch32": 1, "long": 2, "ragged": 3, "mixed": 4, "extend": 4, "prefill": 4}[name]
+    index = {"tiny": 0, "batch32": 1, "long": 2, "ragged": 3, "write": 3, "mixed": 4, "extend": 4, "prefill": 4}[name]
     wl = workloads.config(index)
     stream = torch.cuda.current_stream(dev)
     t_setup = time.perf_counter()
@@ -475,6 +539,30 @@ def main():
                  "pages_per_split": plan[0], "num_splits": plan[1], "cache_copies_rotated": copies,
                  "fused_append": bool(wl.append)}
         tokens_per_step = wl.batch
+    elif name == "write":
+        # quantize-on-write of a whole cache: the ragged batch's 495,439 cached tokens x 8 kv heads,
+        # bf16 K and V, into a fresh NVFP4 pool at the page table's slots (misaligned sequence starts);
+        # the per-tensor scales are computed once beforehand, as a prefill would
+        k, v, slots = (torch.cat([wl.kv("k", b) for b in range(wl.batch)]).to(dev),
+                       torch.cat([wl.kv("v", b) for b in range(wl.batch)]).to(dev),
+                       torch.from_numpy(np.concatenate([wl.slots(b) for b in range(wl.batch)])).to(dev))
+        n_tok = k.shape[0]
+        g_k, g_v = nv.global_scale(k), nv.global_scale(v)
+        gk, gv = float(g_k.item()), float(g_v.item())
+        pool = nv.alloc_nvfp4_pool(wl.num_pages, wl.h_kv, dev)
+        call = nv.prepare_nvfp4_quantize_append(k, v, slots, gk, gv, pool)
+        log(f"write inputs ready in {time.perf_counter() - t_setup:.1f} s")
+
+        def step(events=None, i=0):
+            call.run()
+        # reads 2 x 256 B of bf16 and writes 2 x 72 B per (token, kv head)
+        step_bytes = n_tok * wl.h_kv * (512 + 144)
+        timed_kernel = None
+        kernel_bytes = None
+        desc = (f"write: NVFP4 quantize-on-write of {n_tok} tokens x {wl.h_kv} kv heads (the ragged batch's cache, "
+                f"bf16 K and V) into a paged pool")
+        extra = {"tokens": n_tok, "kv_heads": wl.h_kv, "head_dim": 128, "page_size": 16, "sequences": wl.batch}
+        tokens_per_step = n_tok
     elif name == "mixed":
         pt = torch.from_numpy(wl.page_table).to(dev)
         sl = torch.from_numpy(wl.total_lens.astype(np.int32)).to(dev)
@@ -680,6 +768,24 @@ def main():
         f"{value:.1f} GB/s ({value / HBM_PEAK_GBS:.1%} of 8 TB/s); {timed_kernel} {kernel_ms * 1e3:.1f} us "
         f"-> {achieved:.1f} {unit} ({achieved / peak:.1%} of {peak:.0f})")
 
+    gscale = None
+    if name == "write":
+        # the per-tensor scale reduction over the same K and V (amax of 2 x 1.01 GB of bf16), timed apart
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nv.global_scale(k, out=g_k)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            nv.global_scale(k, out=g_k)
+            nv.global_scale(v, out=g_v)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gb = 2 * n_tok * wl.h_kv * 128 * 2
+        assert (float(g_k.item()), float(g_v.item())) == (gk, gv)
+        gscale = {"us_for_k_and_v": round(us, 2), "bytes": gb, "GB/s": round(gb / (us * 1e-6) / 1e9, 1)}
+        log(f"global scale of K and V: {us:.1f} us, {gscale['GB/s']} GB/s")
+
     # the device's streaming-read rate, for the decode configs (after the timed region)
     ceiling = None
     if bound == "hbm":
@@ -690,6 +796,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and name in ("long", "batch32", "ragged", "tiny"):
         cpu = cpu_baseline(index)
+        log(f"cpu baseline {cpu['value']} GB/s")
+    elif not args.no_cpu_baseline and name == "write":
+        cpu = cpu_baseline_write(index)
         log(f"cpu baseline {cpu['value']} GB/s")
     elif not args.no_cpu_baseline and name in ("mixed", "extend", "prefill"):
         # mixed: the untimed cache preparation (quantizing each unit's K/V) takes ~25x the timed decode,
@@ -735,6 +844,8 @@ def main():
                      "traffic_detail": traffic_detail, "timing": timing},
         "cpu_baseline": cpu,
     }
+    if gscale is not None:
+        res["global_scale"] = gscale
     if ceiling is not None:
         res["stream_read_ceiling"] = ceiling
         res["pct_of_stream_read_ceiling"] = round(100.0 * value / ceiling["value"], 2)

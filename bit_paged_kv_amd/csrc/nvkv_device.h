@@ -86,12 +86,22 @@ __device__ __forceinline__ uint32_t e2m1_encode_mag(float a) {
   return 7u;
 }
 
-// Block scale of a 16-value block with absolute maximum `amax`: returns the E4M3 byte and the
-// fp32 divisor fp32(s * g) of its elements (0 when the scale rounds to zero).
+// Block scale of a 16-value block with absolute maximum `amax`: returns the E4M3 byte of
+// fp32(amax / fp32(6 g)) and the fp32 divisor fp32(s * g) of its elements (0 when the scale rounds
+// to zero).  The quotient is taken as amax * rcp(6 g) (v_rcp_f32: within 1 ulp), within 3 ulps of
+// the correctly rounded one; as in e4m3x4_div, the two can give different E4M3 bytes only next to
+// a rounding midpoint of the normal range or in the subnormal range, and there (or for 6 g outside
+// [2^-100, 2^100], or a NaN quotient) the lane divides.  The byte comes from the pack convert,
+// after the clamp to 448 that gives the encoder's saturation (and NaN -> 0x7E).
 __device__ __forceinline__ uint32_t nvfp4_block_scale(float amax, float g, float* den) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
   const float six_g = 6.0f * g;
-  const float u = amax / six_g;                    // correctly rounded fp32 division
-  const uint32_t sc = e4m3_encode(u);              // u >= 0: sign bit clear
+  float u = amax * __builtin_amdgcn_rcpf(six_g);
+  const uint32_t key = (__float_as_uint(u) & 0xFFFFFu) - (0x80000u - 8u);
+  if (key <= 16u || (u < 0.015625f && u != 0.0f) || !(u == u) || !(six_g >= 0x1p-100f && six_g <= 0x1p100f))
+    u = amax / six_g;                              // correctly rounded fp32 division
+  const v2s w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s){0, 0}, fminf(u, 448.0f), 0.0f, 1.0f, false);
+  const uint32_t sc = __builtin_bit_cast(uint32_t, w) & 0xFFu;   // u >= 0: sign bit clear
   *den = e4m3_value(sc) * g;
   return sc;
 }
@@ -110,12 +120,14 @@ __device__ __forceinline__ uint32_t nvfp4_code(float x, float den) {
 //  * gfx950's v_cvt_scalef32_pk_fp4_f32 with scale 1.0 rounds an fp32 value to E2M1 exactly like the
 //    encoder above (nearest, ties to the even code, saturating, sign kept; checked on the device for
 //    every non-NaN fp32 bit pattern);
-//  * for den in [2^-100, 2^100], q0 = x * fp32(1 / den) is within 3 ulps of fp32(x / den) (two
-//    roundings of relative size <= 2^-24 each), so the two can round to different E2M1 codes only if
-//    an E2M1 rounding threshold (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5: fp32 values whose low 21
-//    significand bits are zero) lies within 3 ulps of q0.  A block with such a value, or with den
-//    outside that range, takes the correctly rounded division for all 16 values.  den == 0 (the
-//    block scale rounded to zero) gives signed zero codes through q = x * 0.
+//  * for den in [2^-100, 2^100], q0 = x * rcp(den) (v_rcp_f32, within 1 ulp of 1 / den) is within 3
+//    ulps of fp32(x / den), so the two can round to different E2M1 codes only if an E2M1 rounding
+//    threshold (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) lies within 3 ulps of q0.  The test: the codes
+//    of the floats 8 bit patterns below and above q0 agree (E2M1 rounding is monotonic in the
+//    magnitude, and so in the pattern within one sign), so no threshold lies between them.  A
+//    block where they differ for some value, or with den outside that range, takes the correctly
+//    rounded division for all 16 values.  den == 0 (the block scale rounded to zero) gives signed
+//    zero codes through q = x * 0.
 __device__ __forceinline__ uint32_t nvfp4_quantize_block_packed(const float (&x)[16], float g, uint32_t& lo,
                                                                 uint32_t& hi) {
   float a = 0.0f;
@@ -126,17 +138,31 @@ __device__ __forceinline__ uint32_t nvfp4_quantize_block_packed(const float (&x)
   float q[16];
   bool exact = den >= 0x1p-100f && den <= 0x1p100f;
   if (exact) {
-    const float r = 1.0f / den;
-    bool near = false;
+    const float r = __builtin_amdgcn_rcpf(den);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      q[i] = x[i] * r;
-      // bit distance to the nearest multiple of 2^21 (as a pattern), shifted so that the threshold
-      // range [0.25, 5] (patterns 0x3E800000 .. 0x40A00000) starts at 0
-      const uint32_t key = (__float_as_uint(q[i]) & 0x7FFFFFFFu) + (8u - 0x3E800000u);
-      near |= key <= 0x02200010u && (key & 0x1FFFFFu) <= 16u;
-    }
-    exact = !near;
+    for (int i = 0; i < 16; ++i) q[i] = x[i] * r;
+    // codes of the patterns 8 below / 8 above each q0 (q0 = +-0 wraps to a NaN pattern below,
+    // which at worst sends the block to the division)
+    uint32_t lo0 = 0, lo1 = 0, hi0 = 0, hi1 = 0;
+    auto dn = [&](int i) { return __uint_as_float(__float_as_uint(q[i]) - 8u); };
+    auto up = [&](int i) { return __uint_as_float(__float_as_uint(q[i]) + 8u); };
+    lo0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo0, dn(0), dn(1), 1.0f, 0);
+    lo0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo0, dn(2), dn(3), 1.0f, 1);
+    lo0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo0, dn(4), dn(5), 1.0f, 2);
+    lo0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo0, dn(6), dn(7), 1.0f, 3);
+    lo1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo1, dn(8), dn(9), 1.0f, 0);
+    lo1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo1, dn(10), dn(11), 1.0f, 1);
+    lo1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo1, dn(12), dn(13), 1.0f, 2);
+    lo1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo1, dn(14), dn(15), 1.0f, 3);
+    hi0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi0, up(0), up(1), 1.0f, 0);
+    hi0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi0, up(2), up(3), 1.0f, 1);
+    hi0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi0, up(4), up(5), 1.0f, 2);
+    hi0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi0, up(6), up(7), 1.0f, 3);
+    hi1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi1, up(8), up(9), 1.0f, 0);
+    hi1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi1, up(10), up(11), 1.0f, 1);
+    hi1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi1, up(12), up(13), 1.0f, 2);
+    hi1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi1, up(14), up(15), 1.0f, 3);
+    exact = lo0 == hi0 && lo1 == hi1;
   }
   if (!exact) {
 #pragma unroll

@@ -156,6 +156,39 @@ def test_nvfp4_quantize_near_rounding_thresholds_bitexact(nv):
     assert cases > 800
 
 
+@pytest.mark.parametrize("k", [0, 1, -1, 2, -2, 3, -3, 6, -9])
+def test_nvfp4_block_scale_near_e4m3_midpoints_bitexact(nv, k):
+    """Block maxima on every E4M3 value and rounding midpoint (normal and subnormal) and past the
+    448 saturation, under global scales with fp32(6 g) = 1 and a few ulps off it, so that the
+    scale quotients amax / fp32(6 g) sit on, or ulps beside, every E4M3 rounding decision: scale
+    bytes and codes must be those of the correctly rounded quotient (one launch per scale)."""
+    pos = o_codecs.E4M3_POSITIVE
+    mids = (pos[:-1] + pos[1:]) / 2
+    amaxes = np.concatenate([pos[1:], mids, [448.0, 464.0, 480.0, 512.0, 960.0, 2.0 ** -10, 3 * 2.0 ** -11]])
+    n_tok = -(-amaxes.size // 8)
+    amaxes = np.concatenate([amaxes, np.ones(n_tok * 8 - amaxes.size)]).astype(np.float32)
+    pattern = np.array([1.0, 0.5, -0.25, 0.75, -1.0, 0.375, -0.625, 0.0, 0.125, -0.875, 0.5, 0.25, -0.75, 0.875,
+                        -0.5, 0.0625], np.float32)   # |max| = 1 at positions 0 and 4; <= 3 significant bits each
+    tok = (amaxes[:, None] * pattern[None, :]).reshape(n_tok, 1, 128).astype(np.float32)
+    assert np.array_equal(_bf16(tok).float().numpy(), tok)         # every value exact in bf16
+    g = np.float32(np.float32(1.0 + k * 2.0 ** -23) / np.float32(6.0))
+    six_g = np.float32(np.float32(6.0) * g)
+    assert abs(float(six_g) - 1.0) <= 16 * 2.0 ** -23
+    slots = np.arange(n_tok, dtype=np.int32)
+    pages = -(-n_tok // 16)
+    dshape, sshape = o_layout.nvfp4_pool_shapes(pages, 1)
+    want = {kk: np.zeros(sh, np.uint8) for kk, sh in (("k_data", dshape), ("k_scale", sshape),
+                                                     ("v_data", dshape), ("v_scale", sshape))}
+    c, sc = o_nv.quantize_blocks(tok, g)
+    cn, scn = o_nv.quantize_blocks(-tok, g)
+    o_layout.write_nvfp4_tokens(want["k_data"], want["k_scale"], "k", slots, c, sc)
+    o_layout.write_nvfp4_tokens(want["v_data"], want["v_scale"], "v", slots, cn, scn)
+    pool = nv.alloc_nvfp4_pool(pages, 1, DEV)
+    tt = _bf16(tok).to(DEV)
+    nv.nvfp4_quantize_append(tt, -tt, torch.from_numpy(slots).to(DEV), float(g), float(g), pool)
+    _check_pool(pool, want)
+
+
 def test_nvfp4_quantize_fp8_input_bitexact(nv):
     rng = np.random.default_rng(9)
     n_tok, h = 40, 2
