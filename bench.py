@@ -2,7 +2,7 @@
 """Benchmark: NVFP4 paged decode attention on one MI355X -- effective KV GB/s (% of HBM peak) + tokens/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config long|batch32|ragged|mixed|extend|prefill|write|tiny|sweep]
+                    [--config long|batch32|ragged|mixed|extend|prefill|write|gather|tiny|sweep]
 
 One step is one decode step of the workload's hot path, inputs already resident in HBM:
   long     split-K NVFP4 decode + log-sum-exp merge, 4 x 131072 tokens, 8 KV / 64 query heads (default)
@@ -16,6 +16,7 @@ One step is one decode step of the workload's hot path, inputs already resident 
            over the copy
   write    quantize-on-write of the ragged batch's whole cache (495,439 tokens x 8 kv heads, bf16 K
            and V) into a fresh NVFP4 pool; the per-tensor scale reduction is timed apart
+  gather   the extend path's prefix gather alone: one NVFP4 layer's 16384-token prefix -> FP8 workspace
   tiny     1 x 256 tokens (latency-bound)
   sweep    precision studies (per-layer NVFP4 vs FP8 sensitivity, per-tensor scale variants)
 
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="long", choices=["long", "batch32", "ragged", "mixed", "extend", "prefill",
-                                                         "write", "tiny", "sweep"])
+                                                         "write", "gather", "tiny", "sweep"])
     ap.add_argument("--pages-per-split", type=int, default=0, help="force the split size (0 = planner)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -397,6 +398,61 @@ def cpu_baseline_write(cfg_index, budget_s=6.0):
                       f"{platform.processor() or platform.machine()}"}
 
 
+def _cpu_gather_units(args):
+    """One pool worker, prefix gather: the oracle's NVFP4 -> FP8 workspace transcode of K and V on
+    (layer, kv head) units of the extend prefix; returns (bytes as the kernel counts them, seconds)."""
+    cfg_index, units, budget_s = args
+    from threadpoolctl import threadpool_limits
+
+    import workloads
+    from oracle import fp8 as o_fp8
+    from oracle import nvfp4 as o_nv
+    wl = workloads.config(cfg_index)
+    prefix = wl.extend_prefix
+    ext = workloads.Workload(name="extend", seed=wl.seed, batch=1, h_kv=wl.h_kv, h_q=wl.h_q,
+                             seq_lens=[prefix + wl.extend_chunk], chan=wl.chan)
+    done_bytes, spent, cur = 0, 0.0, None
+    with threadpool_limits(limits=1):
+        for layer, hk in units:
+            if cur is None or cur[0] != layer:
+                k = ext.kv("k", 0, layer, length=prefix).float().numpy()
+                v = ext.kv("v", 0, layer, length=prefix).float().numpy()
+                cur = (layer, k, v, o_nv.global_scale(k), o_nv.global_scale(v))
+            _, k, v, gk, gv = cur
+            ck, sk = o_nv.quantize_blocks(k[:, hk], gk)              # the cached prefix (not timed)
+            cv, sv = o_nv.quantize_blocks(v[:, hk], gv)
+            t0 = time.perf_counter()
+            o_fp8.nvfp4_to_fp8_workspace(ck, sk, gk, np.float32(6.0 * gk))
+            o_fp8.nvfp4_to_fp8_workspace(cv, sv, gv, np.float32(6.0 * gv))
+            spent += time.perf_counter() - t0
+            done_bytes += prefix * (144 + 256)
+            if spent >= budget_s:
+                break
+    return done_bytes, spent
+
+
+def cpu_baseline_gather(cfg_index, budget_s=6.0):
+    """The oracle's prefix transcode timed on (layer, kv head) units, one unit list per host core (at
+    most 16 spawned workers, ~budget_s of oracle time each); summed GB/s."""
+    import multiprocessing as mp
+
+    import workloads
+    wl = workloads.config(cfg_index)
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    all_units = [(layer, hk) for layer in range(wl.layers) if not wl.is_fp8(layer) for hk in range(wl.h_kv)]
+    n = len(all_units)
+    jobs = [(cfg_index, all_units[w * n // cores:(w + 1) * n // cores], budget_s) for w in range(cores)]
+    with mp.get_context("spawn").Pool(cores) as pool:
+        res = pool.map(_cpu_gather_units, jobs)
+    total = sum(r[0] for r in res)
+    rate = sum(r[0] / r[1] for r in res if r[1] > 0)
+    spent = sum(r[1] for r in res)
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{total} bytes (NVFP4 read, FP8 written) of (layer, kv head) units of the 16384-token extend "
+                      f"prefix (fp32 transcode of K and V), {spent:.1f} s of oracle time over {cores} single-threaded "
+                      f"workers; rate summed over workers; host {platform.processor() or platform.machine()}"}
+
+
 def cpu_baseline_stack(cfg_index, mode, budget_s=6.0, rows=1024):
     """The oracle timed on the mixed stack (mode "mixed", KV GB/s) or on the extend / prefill step of
     its NVFP4 layers (step GB/s, plus the oracle's attention TFLOP/s), one unit list per host core
@@ -494,7 +550,8 @@ def main():
     if name == "sweep":
         precision_studies(nv, workloads, dev)
         return
-    index = {"tiny": 0, "batch32": 1, "long": 2, "ragged": 3, "write": 3, "mixed": 4, "extend": 4, "prefill": 4}[name]
+    index = {"tiny": 0, "batch32": 1, "long": 2, "ragged": 3, "write": 3, "mixed": 4, "extend": 4, "prefill": 4,
+             "gather": 4}[name]
     wl = workloads.config(index)
     stream = torch.cuda.current_stream(dev)
     t_setup = time.perf_counter()
@@ -563,6 +620,36 @@ def main():
                 f"bf16 K and V) into a paged pool")
         extra = {"tokens": n_tok, "kv_heads": wl.h_kv, "head_dim": 128, "page_size": 16, "sequences": wl.batch}
         tokens_per_step = n_tok
+    elif name == "gather":
+        # the extend path's prefix gather alone: one NVFP4 layer's 16384-token prefix (8 kv heads, a
+        # permuted page table) transcoded into the dense FP8 workspace, one launch per step
+        layer = next(l for l in range(wl.layers) if not wl.is_fp8(l))
+        prefix = wl.extend_prefix
+        ext = workloads.Workload(name="extend", seed=wl.seed, batch=1, h_kv=wl.h_kv, h_q=wl.h_q,
+                                 seq_lens=[prefix + wl.extend_chunk], chan=wl.chan)
+        from bit_paged_kv_amd import paged
+        slots = torch.from_numpy(ext.slots(0, 0, prefix)).to(dev)
+        pool, gk_l, gv_l = paged.build_nvfp4_cache(ext.kv("k", 0, layer, length=prefix).to(dev),
+                                                   ext.kv("v", 0, layer, length=prefix).to(dev), slots, ext.num_pages)
+        pt = torch.from_numpy(ext.page_table).to(dev)
+        prefix_lens = torch.tensor([prefix], dtype=torch.int32, device=dev)
+        offs = torch.tensor([0, prefix], dtype=torch.int32, device=dev)
+        k_ws = torch.empty((prefix, wl.h_kv, 128), dtype=torch.uint8, device=dev)
+        v_ws = torch.empty_like(k_ws)
+        call = nv.prepare_dequant_to_workspace(pool, gk_l, gv_l, pt, prefix_lens, offs, prefix, 6.0 * gk_l,
+                                               6.0 * gv_l, wl.h_kv, k_ws, v_ws)
+        log(f"gather inputs ready in {time.perf_counter() - t_setup:.1f} s")
+
+        def step(events=None, i=0):
+            call.run()
+        # reads 2 x 72 B of NVFP4 and writes 2 x 128 B of FP8 per (token, kv head)
+        step_bytes = prefix * wl.h_kv * (144 + 256)
+        timed_kernel = None
+        kernel_bytes = None
+        desc = (f"gather: NVFP4 prefix of {prefix} tokens x {wl.h_kv} kv heads (one layer of the 28-layer stack, "
+                f"permuted pages) -> dense FP8 workspace")
+        extra = {"prefix": prefix, "kv_heads": wl.h_kv, "head_dim": 128, "page_size": 16}
+        tokens_per_step = prefix
     elif name == "mixed":
         pt = torch.from_numpy(wl.page_table).to(dev)
         sl = torch.from_numpy(wl.total_lens.astype(np.int32)).to(dev)
@@ -796,6 +883,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and name in ("long", "batch32", "ragged", "tiny"):
         cpu = cpu_baseline(index)
+        log(f"cpu baseline {cpu['value']} GB/s")
+    elif not args.no_cpu_baseline and name == "gather":
+        cpu = cpu_baseline_gather(index)
         log(f"cpu baseline {cpu['value']} GB/s")
     elif not args.no_cpu_baseline and name == "write":
         cpu = cpu_baseline_write(index)
