@@ -20,6 +20,7 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const uint8_t* __rest
   const size_t nbytes = n * elem_bytes;
   const size_t nvec = nbytes / 16;
   uint32_t m = 0;
+#pragma unroll 4
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += (size_t)gridDim.x * blockDim.x) {
     const uint4 v = reinterpret_cast<const uint4*>(x)[i];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(64 * kWsWaves) void nvfp4_to_fp8_ws_kernel(
 // ---------------------------------------------------------------------------------------------
 // launchers (validated arguments only; called from the C ABI layer)
 // ---------------------------------------------------------------------------------------------
-constexpr int kAmaxBlocks = 1024;
+constexpr int kAmaxBlocks = 2048;   // eight 256-thread workgroups per CU: the streaming-read probe's shape
 
 size_t global_scale_workspace_bytes() { return kAmaxBlocks * sizeof(uint32_t); }
 
