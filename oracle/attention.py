@@ -7,7 +7,7 @@ K/V.  This module is that definition, in fp64:
 
     z_t = sm_scale * <q, K_hat_t>,  p = softmax(z),  o = sum_t p_t V_hat_t
 
-over the sequence's tokens.  Reading R11: query head hq uses KV head
+over the sequence's tokens.  Reading R10: query head hq uses KV head
 hq // (H_q / H_kv) (contiguous GQA groups).  The maximum is subtracted before
 the exponential (it cancels exactly in the ratio).  Matrix products use numpy's
 fp64 routines.

@@ -8,10 +8,10 @@
 
 Readings (repeated in the design notes):
 
-* R14 the FP8 cache is per-tensor scaled: s = fp32(amax / 448); a value is
+* R13 the FP8 cache is per-tensor scaled: s = fp32(amax / 448); a value is
       stored as E4M3(fp32(x / s)) (RNE, saturating, sign kept) and read back as
       e4m3 * s;
-* R15 the workspace uses the FP8 scale of the layer (passed in, ``s_ws``); each
+* R14 the workspace uses the FP8 scale of the layer (passed in, ``s_ws``); each
       prefix value is first dequantized in fp32 -- v = fp32(fp32(e2m1 * s_blk) * g)
       -- then stored as E4M3(fp32(v / s_ws)) with the sign of its E2M1 code.
 """
@@ -26,13 +26,13 @@ FP8_DIVISOR = np.float32(448.0)
 
 
 def fp8_scale(x) -> np.float32:
-    """R14: per-tensor scale s = fp32(max |x| / 448)."""
+    """R13: per-tensor scale s = fp32(max |x| / 448)."""
     a = np.max(np.abs(np.asarray(x, dtype=np.float32)))
     return np.float32(np.float32(a) / FP8_DIVISOR)
 
 
 def fp8_quantize(x, s) -> np.ndarray:
-    """R14: E4M3 byte of fp32(x / s) for every element (RNE, saturating, sign copied)."""
+    """R13: E4M3 byte of fp32(x / s) for every element (RNE, saturating, sign copied)."""
     x = np.asarray(x, dtype=np.float32)
     s = np.float32(s)
     if not (np.isfinite(s) and s > 0):
@@ -46,7 +46,7 @@ def fp8_dequantize(codes, s) -> np.ndarray:
 
 
 def nvfp4_to_fp8_workspace(codes, scale_bytes, g, s_ws) -> np.ndarray:
-    """R15: FP8 workspace bytes for NVFP4 codes [..., D] with block-scale bytes [..., D/16]."""
+    """R14: FP8 workspace bytes for NVFP4 codes [..., D] with block-scale bytes [..., D/16]."""
     codes = np.asarray(codes, dtype=np.uint8)
     d = codes.shape[-1]
     e = e2m1_decode(codes).astype(np.float32)             # exact

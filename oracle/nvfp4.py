@@ -17,9 +17,11 @@ Readings of points the pages leave open (each repeated where it is applied):
       saturation, a = max |x| over the block;
 * R6  element codes come from y = fp32(x / fp32(s * g)) (correctly rounded fp32
       division) rounded to E2M1 by RNE with saturation;
-* R8  the sign bit is copied from x, also when the magnitude rounds to zero;
+* R7  the sign bit is copied from x, also when the magnitude rounds to zero;
       a block whose scale rounds to zero stores signed zeros;
-* R9  element 2i goes to the low nibble of byte i, element 2i+1 to the high one.
+* R8  in the packed form element 2i goes to the low nibble of byte i, element
+      2i+1 to the high one (where each byte sits in a page is the layout's
+      business, see ``layout``).
 """
 
 from __future__ import annotations
@@ -63,7 +65,7 @@ def quantize_blocks(x, g):
 
 
 def _quantize_block_rows(xb, g):
-    """Blocks [n][16] -> (codes [n][16], scale bytes [n]); the steps R5, R6, R8."""
+    """Blocks [n][16] -> (codes [n][16], scale bytes [n]); the steps R5, R6, R7."""
     # R5: block amax -> u = a / fp32(6 g) -> E4M3 (RNE, saturating)
     a = np.max(np.abs(xb), axis=-1)
     six_g = np.float32(np.float32(6.0) * g)
@@ -77,7 +79,7 @@ def _quantize_block_rows(xb, g):
     y = (xb / safe_den[..., None]).astype(np.float32)
     mag = e2m1_encode_magnitude(np.abs(y))
     mag = np.where(zero_scale[..., None], np.uint8(0), mag).astype(np.uint8)
-    # R8: sign copied from x
+    # R7: sign copied from x
     sign = np.signbit(xb).astype(np.uint8) << 3
     return mag | sign, scale_bytes
 
@@ -92,7 +94,7 @@ def dequantize_blocks(codes, scale_bytes, g) -> np.ndarray:
 
 
 def pack_nibbles(codes) -> np.ndarray:
-    """R9: two 4-bit codes per byte, element 2i in the low nibble."""
+    """R8: two 4-bit codes per byte, element 2i in the low nibble."""
     c = np.asarray(codes, dtype=np.uint8)
     return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
 
