@@ -151,6 +151,11 @@ def global_scale(x: torch.Tensor, divisor: float = NVFP4_GLOBAL_DIVISOR, in_scal
 # a2 / a5: quantize-on-write
 # ------------------------------------------------------------------------------------------------
 def _nvfp4_quantize_args(k, v, slots, k_gscale, v_gscale, pool, k_in_scale, v_in_scale):
+    # bf16 values, or E4M3 bytes (uint8) that mean e4m3 * in_scale; any other dtype is an error
+    if not isinstance(k, torch.Tensor) or k.dtype not in (torch.bfloat16, torch.uint8):
+        raise TypeError(f"k must be a bfloat16 or uint8 (E4M3 bytes) tensor, got {getattr(k, 'dtype', type(k))}")
+    if not isinstance(v, torch.Tensor) or v.dtype != k.dtype:
+        raise TypeError(f"v must have k's dtype {k.dtype}, got {getattr(v, 'dtype', type(v))}")
     dt = IN_BF16 if k.dtype == torch.bfloat16 else IN_FP8
     _need(k, k.dtype, "k")
     _need(v, k.dtype, "v")

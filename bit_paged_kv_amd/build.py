@@ -9,7 +9,10 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvkv.so")
 # per-source extra flags.  The decode and extend-attention kernels never see NaN scores (masked
 # keys are -inf, unwritten scales are zeroed), so their max trees need no NaN quieting; the
-# write-side kernels keep strict IEEE semantics for bit-exact quantization.
+# write-side kernels keep strict IEEE semantics for bit-exact quantization.  The decode file also
+# holds the fused append's quantization: from input without NaN its steps produce no NaN (+-inf
+# saturates through fmin and the correctly rounded division), so the flag leaves its bytes equal to
+# the standalone writer's (a GPU test compares the two on inputs with +-inf).
 SOURCES = {"nvkv_quant.hip": [], "nvkv_decode.hip": ["-fno-honor-nans"], "nvkv_extend.hip": [],
            "nvkv_extend_attn.hip": ["-fno-honor-nans"], "nvkv_probe.hip": [],
            "nvkv_api.cpp": []}

@@ -157,7 +157,10 @@ NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_k
  *   pages_per_split, num_splits : from nvkv_plan_decode.
  *   new_k, new_v : NULL, or [batch][num_kv_heads][128] bf16: fused quantize-append of one token
  *                  per sequence at position seq_lens[b] - 1 (its page must be in the page table)
- *                  before attending; uses k_global_scale / v_global_scale.  Both or neither.
+ *                  before attending; uses k_global_scale / v_global_scale.  Both or neither.  The
+ *                  bytes written equal nvfp4_kv_quantize_append's for every input without NaN
+ *                  (+-inf saturates to a 448 block scale and code +-6); NaN input is outside the
+ *                  contract of both writers.
  *   out        : [batch][num_q_heads][128] fp32, device.
  *   workspace  : >= nvkv_decode_workspace_size(...) bytes, device (may be NULL if that is 0).
  */

@@ -249,3 +249,25 @@ def test_read_probe_validation(lib):
     assert p(A, 40, A, S) == INVAL          # not a multiple of 16
     assert p(MIS, 32, A, S) == INVAL
     assert p(A, 32, A + 2, S) == INVAL      # sink not 4-byte aligned
+
+
+@pytest.mark.parametrize("dtype", ["float16", "float32", "int8"])
+def test_quantize_binding_rejects_other_input_dtypes(lib, dtype):
+    """Only bf16 values or E4M3 bytes (uint8) may be quantized; other dtypes raise before any call."""
+    import torch
+    k = torch.zeros((1, 1, 128), dtype=getattr(torch, dtype))
+    pool = {n: torch.zeros((1, 1, 8), dtype=torch.uint8) for n in ("k_data", "k_scale", "v_data", "v_scale")}
+    slots = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        lib.nvfp4_quantize_append(k, k.clone(), slots, 1.0, 1.0, pool)
+    with pytest.raises(TypeError):
+        lib.nvfp4_prefill_write(k, k.clone(), slots, 1.0, 1.0, pool, 1.0, 1.0, k, k)
+
+
+def test_quantize_binding_rejects_mixed_k_v_dtypes(lib):
+    import torch
+    k = torch.zeros((1, 1, 128), dtype=torch.bfloat16)
+    v = torch.zeros((1, 1, 128), dtype=torch.uint8)
+    pool = {n: torch.zeros((1, 1, 8), dtype=torch.uint8) for n in ("k_data", "k_scale", "v_data", "v_scale")}
+    with pytest.raises(TypeError):
+        lib.nvfp4_quantize_append(k, v, torch.zeros(1, dtype=torch.int32), 1.0, 1.0, pool)

@@ -7,6 +7,7 @@ import torch
 import workloads
 from oracle import attention as o_att
 from oracle import fp8 as o_fp8
+from oracle import layout as o_layout
 from oracle import nvfp4 as o_nv
 from tests import helpers as H
 
@@ -36,7 +37,8 @@ def test_decode_tiny(nv):
     ks, vs = H.oracle_inputs(wl)
     gk, gv = H.oracle_nvfp4_scales(wl)
     want = H.oracle_nvfp4_decode(wl, wl.q().float().numpy(), ks, vs, gk, gv)
-    pool, _, _ = H.gpu_nvfp4_layer(wl, 0, DEV, fill=0xFF)   # unused bytes hold NaN scale patterns
+    pool, g_k, g_v = H.gpu_nvfp4_layer(wl, 0, DEV, fill=0xFF)   # unused bytes hold NaN scale patterns
+    assert (np.float32(g_k), np.float32(g_v)) == (gk, gv), "GPU global scales differ from the oracle's"
     for pps in (0, 2, 4, 16):
         got, plan = _run_nvfp4(nv, wl, pool, gk, gv, force_pps=pps)
         H.assert_attention_close(got, want, f"tiny plan={plan}")
@@ -134,6 +136,43 @@ def test_decode_fused_append(nv):
             assert np.array_equal(pool[key].cpu().numpy(), want_pool[key]), key
 
 
+def test_fused_append_infinities_match_standalone_writer(nv):
+    """New tokens holding +-inf and values far past the calibrated range: the decode kernel's fused
+    append (built without NaN semantics) writes the same bytes as nvfp4_kv_quantize_append and as
+    the oracle -- infinities saturate to a 448 block scale and code +-6, no NaN arises."""
+    wl = workloads.Workload(name="append-inf", seed=51, batch=3, h_kv=2, h_q=8, seq_lens=[20, 33, 7],
+                            append=True, extra_pages=1)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    nk = wl.new_token("k").clone()
+    nvv = wl.new_token("v").clone()
+    nk[0, 0, 5] = float("inf")
+    nk[1, 1, 64:80] = float("-inf")
+    nk[2, 0, :16] = 1e30
+    nvv[0, 1, 127] = float("-inf")
+    nvv[2, 1, 40] = float("inf")
+    # oracle bytes of the whole cache + the new tokens
+    ks, vs = H.oracle_inputs(wl, with_new=False)
+    ks = [np.concatenate([k, nk[b:b + 1].float().numpy()]) for b, k in enumerate(ks)]
+    vs = [np.concatenate([v, nvv[b:b + 1].float().numpy()]) for b, v in enumerate(vs)]
+    want_pool = H.oracle_nvfp4_pool(wl, ks, vs, gk, gv, fill=0x11)
+    # fused: decode with new_k / new_v
+    pool_f, g_k, g_v = H.gpu_nvfp4_layer(wl, 0, DEV, fill=0x11)
+    pt, sl = H.gpu_tables(wl, DEV)
+    plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), 0, 2)
+    nv.nvfp4_decode(wl.q().to(DEV), pool_f, g_k, g_v, pt, sl, wl.sm_scale, plan, wl.h_kv, new_k=nk.to(DEV),
+                    new_v=nvv.to(DEV))
+    # standalone writer of the same tokens
+    pool_s, _, _ = H.gpu_nvfp4_layer(wl, 0, DEV, fill=0x11)
+    slots = np.array([wl.page_table[b, int(wl.seq_lens[b]) // 16] * 16 + int(wl.seq_lens[b]) % 16
+                      for b in range(wl.batch)], dtype=np.int32)
+    nv.nvfp4_quantize_append(nk.to(DEV), nvv.to(DEV), torch.from_numpy(slots).to(DEV), g_k, g_v, pool_s)
+    torch.cuda.synchronize()
+    for key in ("k_data", "k_scale", "v_data", "v_scale"):
+        f, st = pool_f[key].cpu().numpy(), pool_s[key].cpu().numpy()
+        assert np.array_equal(f, st), f"{key}: fused append differs from the standalone writer"
+        assert np.array_equal(f, want_pool[key]), f"{key}: differs from the oracle"
+
+
 def _fp8_case(wl, layer=0):
     ks, vs = H.oracle_inputs(wl, layer)
     sk = o_fp8.fp8_scale(np.concatenate(ks))
@@ -142,10 +181,12 @@ def _fp8_case(wl, layer=0):
     return want, sk, sv
 
 
-def test_fp8_decode(nv):
+@pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
+def test_fp8_decode(nv, group):
+    """FP8 layers across GQA groups: 1..8 use the packed hi/lo kernel, 16 the two-product one."""
     from bit_paged_kv_amd import paged
-    wl = workloads.Workload(name="fp8", seed=60, batch=4, h_kv=2, h_q=8, seq_lens=[1, 17, 300, 1029],
-                            chan="outlier2", extra_pages=2)
+    wl = workloads.Workload(name=f"fp8-g{group}", seed=60 + group, batch=4, h_kv=2, h_q=2 * group,
+                            seq_lens=[1, 17, 300, 1029], chan="outlier2", extra_pages=2)
     want, sk, sv = _fp8_case(wl)
     k, v, slots = H.gpu_all_tokens(wl, 0, DEV)
     pool, g_sk, g_sv = paged.build_fp8_cache(k, v, slots, wl.num_pages, fill=0xFF)
@@ -194,6 +235,26 @@ def test_decode_layers_mixed_stack(nv):
             assert torch.equal(L["out"], first[i]), f"prepared layer {i}"
 
 
+def _pool_rows(pool, wl, b, hk, n_tok):
+    """The pages of stream (b, hk) that hold its first n_tok tokens, copied to the host in sequence
+    order: {key: [pages][1][bytes]}, so that token t sits at local slot t."""
+    pages = torch.from_numpy(wl.page_table[b, :(n_tok + 15) // 16].astype(np.int64)).to(DEV)
+    return {key: t[pages, hk:hk + 1].cpu().numpy() for key, t in pool.items()}
+
+
+def _assert_nvfp4_rows(rows, ck, sk, cv, sv, tag):
+    """Every code and scale byte of one stream's tokens equals the oracle's."""
+    n = ck.shape[0]
+    local = np.arange(n)
+    gck, gsk = o_layout.read_nvfp4_tokens(rows["k_data"], rows["k_scale"], "k", local)
+    gcv, gsv = o_layout.read_nvfp4_tokens(rows["v_data"], rows["v_scale"], "v", local)
+    for name, got, want in (("K codes", gck[:, 0], ck), ("K scales", gsk[:, 0], sk), ("V codes", gcv[:, 0], cv),
+                            ("V scales", gsv[:, 0], sv)):
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{tag}: {name} differ at {len(bad)} places, first (token, index) {bad[0].tolist()}"
+    print(f"{tag}: {n} tokens' codes and scales bit-exact", flush=True)
+
+
 def _sampled_full_size(nv, index, samples):
     """Full-size workload in the bench's launch configuration; the oracle recomputes the sampled
     (sequence, kv head) rows from the same seeded inputs (never from anything the GPU produced)."""
@@ -215,6 +276,8 @@ def _sampled_full_size(nv, index, samples):
     nvv = wl.new_token("v") if fused else None
     out = nv.nvfp4_decode(q.to(DEV), pool, gk, gv, pt, sl, wl.sm_scale, plan, wl.h_kv,
                           new_k=nk.to(DEV) if fused else None, new_v=nvv.to(DEV) if fused else None).cpu().numpy()
+    # the sampled streams' pages as the step left them (the appended token included)
+    rows = {(b, hk): _pool_rows(pool, wl, b, hk, int(wl.total_lens[b])) for b, hk in samples}
     del pool
     torch.cuda.empty_cache()
     print(f"cfg{index}: GPU step done, plan {plan}", flush=True)
@@ -232,6 +295,7 @@ def _sampled_full_size(nv, index, samples):
             v = np.concatenate([v, nvv[b, hk][None].float().numpy()])
         ck, sk = o_nv.quantize_blocks(k, ogk)
         cv, sv = o_nv.quantize_blocks(v, ogv)
+        _assert_nvfp4_rows(rows[(b, hk)], ck, sk, cv, sv, f"cfg{index} b={b} hk={hk}")
         kh = o_nv.dequantize_blocks(ck, sk, ogk)[:, None]
         vh = o_nv.dequantize_blocks(cv, sv, ogv)[:, None]
         want = o_att.decode_attention_one(qf[b, hk * G:(hk + 1) * G], kh, vh, wl.sm_scale)
@@ -289,6 +353,9 @@ def test_full_size_mixed_stack_sampled(nv):
         print(f"mixed full size: layer {layer} cache built", flush=True)
     outs = [o.cpu().numpy() for o in nv.decode_layers(layers, pt, sl, wl.sm_scale, plan, wl.h_kv)]
     print(f"mixed full size: GPU step done, plan {plan}", flush=True)
+    samples = [(0, 0), (21, 5), (43, 7)]
+    rows = {(i, b, hk): _pool_rows(L["pool"], wl, b, hk, int(wl.total_lens[b]))
+            for i, L in enumerate(layers) for b, hk in samples}
     del layers
     torch.cuda.empty_cache()
     G = wl.group
@@ -301,15 +368,23 @@ def test_full_size_mixed_stack_sampled(nv):
         else:
             ok, ov = o_nv.global_scale(amax_k), o_nv.global_scale(amax_v)
         assert (np.float32(s1), np.float32(s2)) == (ok, ov), f"layer {layer} scales"
-        for b, hk in [(0, 0), (21, 5), (43, 7)]:
+        for b, hk in samples:
             k = ks[b][:, hk].float().numpy()
             v = vs[b][:, hk].float().numpy()
+            r = rows[(i, b, hk)]
+            tag = f"mixed layer {layer} b={b} hk={hk}"
             if fp8:
-                kh = o_fp8.fp8_dequantize(o_fp8.fp8_quantize(k, ok), ok)[:, None]
-                vh = o_fp8.fp8_dequantize(o_fp8.fp8_quantize(v, ov), ov)[:, None]
+                bk, bv = o_fp8.fp8_quantize(k, ok), o_fp8.fp8_quantize(v, ov)
+                local = np.arange(k.shape[0])
+                assert np.array_equal(o_layout.read_fp8_tokens(r["k"], "k", local)[:, 0], bk), f"{tag}: K bytes"
+                assert np.array_equal(o_layout.read_fp8_tokens(r["v"], "v", local)[:, 0], bv), f"{tag}: V bytes"
+                print(f"{tag}: {k.shape[0]} tokens' FP8 bytes bit-exact", flush=True)
+                kh = o_fp8.fp8_dequantize(bk, ok)[:, None]
+                vh = o_fp8.fp8_dequantize(bv, ov)[:, None]
             else:
                 ck, sk = o_nv.quantize_blocks(k, ok)
                 cv, sv = o_nv.quantize_blocks(v, ov)
+                _assert_nvfp4_rows(r, ck, sk, cv, sv, tag)
                 kh = o_nv.dequantize_blocks(ck, sk, ok)[:, None]
                 vh = o_nv.dequantize_blocks(cv, sv, ov)[:, None]
             want = o_att.decode_attention_one(qf[b, hk * G:(hk + 1) * G], kh, vh, wl.sm_scale)
