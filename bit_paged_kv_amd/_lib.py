@@ -50,6 +50,9 @@ EXPORTED = {
                                      _p, _p, _p, _p, _sz, _p]),
     "nvfp4_paged_decode_attn_timed": (_i, [_p, _p, _p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i,
                                            _p, _p, _p, _p, _sz, _p, _p, _p]),
+    "nvkv_decode_noalloc_max_bytes": (_sz, []),
+    "nvfp4_paged_decode_attn_noalloc": (_i, [_p, _p, _p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i,
+                                             _p, _p, _p, _p]),
     "fp8_paged_decode_attn": (_i, [_p, _p, _p, _f, _f, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p, _p, _sz, _p]),
     "nvkv_decode_layers": (_i, [_p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p, _sz, _p]),
     "nvfp4_dequant_to_workspace": (_i, [_p, _p, _p, _p, _f, _f, _p, _i, _p, _p, _i, _i, _i, _i, _i, _f, _f, _p, _p,
@@ -271,6 +274,38 @@ def nvfp4_decode(q: torch.Tensor, pool: dict, k_gscale: float, v_gscale: float, 
         _ptr(q), _ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]), _ptr(pool["v_scale"]),
         k_gscale, v_gscale, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), b, hq, num_kv_heads, HEAD_DIM,
         PAGE_SIZE, sm_scale, pps, ns, _ptr(new_k), _ptr(new_v), _ptr(out), _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def decode_noalloc_max_bytes() -> int:
+    """Size of the library-held split-partial array the no-allocation decode uses (per device)."""
+    return _lib.nvkv_decode_noalloc_max_bytes()
+
+
+def nvfp4_decode_noalloc(q: torch.Tensor, pool: dict, k_gscale: float, v_gscale: float, page_table: torch.Tensor,
+                         seq_lens: torch.Tensor, sm_scale: float, plan, num_kv_heads: int, new_k=None, new_v=None,
+                         out=None) -> torch.Tensor:
+    """nvfp4_decode through nvfp4_paged_decode_attn_noalloc: no workspace, the library's own array holds
+    the split partials (calls overlapping on one device race)."""
+    _need(q, torch.bfloat16, "q")
+    _need(page_table, torch.int32, "page_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch][H_q][128]")
+    b, hq, _ = q.shape
+    if page_table.dim() != 2 or page_table.shape[0] != b or seq_lens.numel() != b:
+        raise ValueError("page_table must be [batch][max_pages] and seq_lens [batch]")
+    if out is None:
+        out = torch.empty((b, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    if new_k is not None:
+        _need(new_k, torch.bfloat16, "new_k")
+        _need(new_v, torch.bfloat16, "new_v")
+    pps, ns = plan
+    _check("nvfp4_paged_decode_attn_noalloc", _lib.nvfp4_paged_decode_attn_noalloc(
+        _ptr(q), _ptr(pool["k_data"]), _ptr(pool["k_scale"]), _ptr(pool["v_data"]), _ptr(pool["v_scale"]),
+        k_gscale, v_gscale, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), b, hq, num_kv_heads, HEAD_DIM,
+        PAGE_SIZE, sm_scale, pps, ns, _ptr(new_k), _ptr(new_v), _ptr(out), _stream(q)))
     return out
 
 

@@ -57,10 +57,10 @@ int device_cus() {
   return n;
 }
 
-int decode_common_status(const void* q, const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens,
-                         int batch, int num_q_heads, int num_kv_heads, int head_dim, int page_size, float sm_scale,
-                         int pages_per_split, int num_splits, const float* out, const void* workspace,
-                         size_t workspace_bytes) {
+// Decode arguments other than the pools and the workspace.
+int decode_args_status(const void* q, const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens,
+                       int batch, int num_q_heads, int num_kv_heads, int head_dim, int page_size, float sm_scale,
+                       int pages_per_split, int num_splits, const float* out) {
   int st = shape_status(head_dim, page_size);
   if (st) return st;
   st = heads_status(num_q_heads, num_kv_heads);
@@ -71,9 +71,31 @@ int decode_common_status(const void* q, const int32_t* page_table, int max_pages
   if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return NVKV_E_INVAL;
   if (pages_per_split < 1 || num_splits < 1) return NVKV_E_INVAL;
   if ((long long)num_splits * batch * num_kv_heads > 0x7FFFFFFFLL) return NVKV_E_INVAL;   // one grid axis
+  return NVKV_OK;
+}
+
+int decode_common_status(const void* q, const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens,
+                         int batch, int num_q_heads, int num_kv_heads, int head_dim, int page_size, float sm_scale,
+                         int pages_per_split, int num_splits, const float* out, const void* workspace,
+                         size_t workspace_bytes) {
+  int st = decode_args_status(q, page_table, max_pages_per_seq, seq_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                              page_size, sm_scale, pages_per_split, num_splits, out);
+  if (st) return st;
   const size_t need = nvkv::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return NVKV_E_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return NVKV_E_INVAL;
+  return NVKV_OK;
+}
+
+// The NVFP4 pools, global scales and fused-append inputs of a decode call.
+int nvfp4_pool_status(const uint8_t* k_data, const uint8_t* k_scale, const uint8_t* v_data, const uint8_t* v_scale,
+                      float k_global_scale, float v_global_scale, const void* new_k, const void* new_v) {
+  if (!k_data || !k_scale || !v_data || !v_scale) return NVKV_E_INVAL;
+  if (!aligned(k_data, 16) || !aligned(k_scale, 16) || !aligned(v_data, 16) || !aligned(v_scale, 16))
+    return NVKV_E_INVAL;
+  if (!good_scale(k_global_scale) || !good_scale(v_global_scale)) return NVKV_E_INVAL;
+  if ((new_k == nullptr) != (new_v == nullptr)) return NVKV_E_INVAL;
+  if (new_k && (!aligned(new_k, 16) || !aligned(new_v, 16))) return NVKV_E_INVAL;
   return NVKV_OK;
 }
 
@@ -88,6 +110,7 @@ const char* nvkv_status_string(int status) {
     case NVKV_E_UNSUPPORTED: return "unsupported shape (head_dim must be 128, page_size 16, GQA group 1..16)";
     case NVKV_E_LAUNCH: return "HIP launch or device query failed";
     case NVKV_E_WORKSPACE: return "workspace missing or too small";
+    case NVKV_E_SCRATCH: return "split partials exceed the library-held scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -218,12 +241,8 @@ int nvfp4_paged_decode_attn_timed(const void* q, const uint8_t* k_data, const ui
                                 head_dim, page_size, sm_scale, pages_per_split, num_splits, out, workspace,
                                 workspace_bytes);
   if (st) return st;
-  if (!k_data || !k_scale || !v_data || !v_scale) return NVKV_E_INVAL;
-  if (!aligned(k_data, 16) || !aligned(k_scale, 16) || !aligned(v_data, 16) || !aligned(v_scale, 16))
-    return NVKV_E_INVAL;
-  if (!good_scale(k_global_scale) || !good_scale(v_global_scale)) return NVKV_E_INVAL;
-  if ((new_k == nullptr) != (new_v == nullptr)) return NVKV_E_INVAL;
-  if (new_k && (!aligned(new_k, 16) || !aligned(new_v, 16))) return NVKV_E_INVAL;
+  st = nvfp4_pool_status(k_data, k_scale, v_data, v_scale, k_global_scale, v_global_scale, new_k, new_v);
+  if (st) return st;
   nvkv::DecodeArgs a{};
   a.format = nvkv::kFmtNvfp4;
   a.q = q;
@@ -248,6 +267,33 @@ int nvfp4_paged_decode_attn_timed(const void* q, const uint8_t* k_data, const ui
   a.workspace = workspace;
   return launch_status(nvkv::launch_decode(a, stream, split_start, split_stop));
 }
+
+int nvfp4_paged_decode_attn_noalloc(const void* q, const uint8_t* k_data, const uint8_t* k_scale,
+                                    const uint8_t* v_data, const uint8_t* v_scale, float k_global_scale,
+                                    float v_global_scale, const int32_t* page_table, int max_pages_per_seq,
+                                    const int32_t* seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int page_size, float sm_scale, int pages_per_split, int num_splits,
+                                    const void* new_k, const void* new_v, float* out, hipStream_t stream) {
+  // every argument is checked before the scratch array is resolved (the first device call)
+  int st = decode_args_status(q, page_table, max_pages_per_seq, seq_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                              page_size, sm_scale, pages_per_split, num_splits, out);
+  if (st) return st;
+  st = nvfp4_pool_status(k_data, k_scale, v_data, v_scale, k_global_scale, v_global_scale, new_k, new_v);
+  if (st) return st;
+  const size_t need = nvkv::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, num_splits);
+  if (need > nvkv::kDecodeScratchBytes) return NVKV_E_SCRATCH;
+  void* scratch = nullptr;
+  if (need > 0 && nvkv::decode_scratch(&scratch) != hipSuccess) {
+    (void)hipGetLastError();
+    return NVKV_E_LAUNCH;
+  }
+  return nvfp4_paged_decode_attn_timed(q, k_data, k_scale, v_data, v_scale, k_global_scale, v_global_scale,
+                                       page_table, max_pages_per_seq, seq_lens, batch, num_q_heads, num_kv_heads,
+                                       head_dim, page_size, sm_scale, pages_per_split, num_splits, new_k, new_v, out,
+                                       scratch, need > 0 ? nvkv::kDecodeScratchBytes : 0, stream, nullptr, nullptr);
+}
+
+size_t nvkv_decode_noalloc_max_bytes(void) { return nvkv::kDecodeScratchBytes; }
 
 int fp8_paged_decode_attn(const void* q, const uint8_t* k_cache, const uint8_t* v_cache, float k_scale, float v_scale,
                           const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens, int batch,

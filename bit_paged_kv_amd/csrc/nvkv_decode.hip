@@ -17,6 +17,8 @@
 //  * online softmax in the exp2 domain with wave butterfly reductions; P enters PV as an fp16
 //    hi + lo pair so that it keeps ~22 significant bits; accumulation is fp32;
 //  * splits write unnormalised partial outputs + (max, sum); a second kernel merges them.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -652,6 +654,34 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restri
 size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits) {
   (void)hkv;
   return num_splits > 1 ? (size_t)batch * hq * num_splits * (kHeadDim + 2) * sizeof(float) : 0;
+}
+
+// Library-held split partials for callers that cannot allocate: one array per device, reached by
+// the kernels only through the device address hipGetSymbolAddress returns (the array's name is a
+// host-side stand-in in this code).  The partials are written before they are read, so the array
+// needs no clearing; calls that overlap on one device share it and race.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::atomic<void*> cache[kMaxScratchDevices];
+  static std::mutex lock;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> g(lock);
+    p = cache[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // this device is current
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      cache[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {

@@ -60,6 +60,14 @@ struct DecodeArgs {
 };
 
 size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits);
+
+// Split partials held by the library for the no-allocation decode entry point: a 32 MiB array per
+// device, room for 64,527 (query row, split) partials of 130 floats (e.g. 64 sequences x 64 query
+// heads x 15 splits); its device address is resolved once per device.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+constexpr int kMaxScratchDevices = 64;
+// Device address of the current device's array (hipGetSymbolAddress, cached per device).
+hipError_t decode_scratch(void** ptr);
 // start / stop (may be null) are recorded by the split kernel's own dispatch.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start = nullptr,
                          hipEvent_t stop = nullptr);

@@ -31,7 +31,8 @@
  * In NVFP4 V data two tokens (o even and o+1) share each byte; writers update single nibbles.
  *
  * CONVENTIONS.  All pointers are device pointers unless stated; the caller owns all memory; the
- * library allocates and frees nothing and keeps no state besides a per-device CU-count cache.
+ * library allocates and frees nothing and keeps no state besides a per-device CU-count cache and,
+ * for nvfp4_paged_decode_attn_noalloc only, one library-held scratch array per device.
  * Every call enqueues work on `stream` and returns without synchronizing.  Calls return an
  * NVKV_* status; nothing is thrown.  Host-side validation covers null pointers, alignment (16 B
  * for pools, q, out and workspace; 4 B for int arrays), shapes, group size and scalar scales.
@@ -60,7 +61,8 @@ enum {
   NVKV_E_INVAL = -1,        /* bad argument (null pointer, misalignment, negative size, bad scale) */
   NVKV_E_UNSUPPORTED = -2,  /* shape outside what the kernels implement (head_dim != 128, page != 16, group > 16) */
   NVKV_E_LAUNCH = -3,       /* a HIP launch or device query failed */
-  NVKV_E_WORKSPACE = -4     /* workspace missing or smaller than the size query returns */
+  NVKV_E_WORKSPACE = -4,    /* workspace missing or smaller than the size query returns */
+  NVKV_E_SCRATCH = -5       /* the no-allocation decode needs more than the library-held scratch */
 };
 
 /* ---- input element types ---- */
@@ -191,6 +193,31 @@ NVKV_API int nvfp4_paged_decode_attn_timed(const void* q,
                             const void* new_k, const void* new_v,
                             float* out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                             hipEvent_t split_start, hipEvent_t split_stop);
+
+/*
+ * nvfp4_paged_decode_attn_noalloc -- nvfp4_paged_decode_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that forbid hipMalloc): the
+ * split partials live in a library-held array of nvkv_decode_noalloc_max_bytes() bytes (32 MiB) per
+ * device instead of a caller workspace, so nothing is allocated.  The caller still passes q, the
+ * pools, the tables and out.  Arguments, results and the other errors as nvfp4_paged_decode_attn.
+ *   Returns NVKV_E_SCRATCH when nvkv_decode_workspace_size(batch, num_q_heads, num_kv_heads, 128,
+ *   num_splits) exceeds nvkv_decode_noalloc_max_bytes(); NVKV_E_LAUNCH if the array's device address
+ *   cannot be resolved (done once per device, on the first call with that device current).
+ *   Every call on a device shares that device's array (it keeps the last call's partials, which the
+ *   kernels overwrite before reading): calls that overlap on one device -- concurrent streams or
+ *   threads -- race and must be serialised by the caller.  The array stays allocated on each device
+ *   the library ran on until the process ends.
+ */
+NVKV_API size_t nvkv_decode_noalloc_max_bytes(void);
+NVKV_API int nvfp4_paged_decode_attn_noalloc(const void* q,
+                            const uint8_t* k_data, const uint8_t* k_scale,
+                            const uint8_t* v_data, const uint8_t* v_scale,
+                            float k_global_scale, float v_global_scale,
+                            const int32_t* page_table, int max_pages_per_seq, const int32_t* seq_lens,
+                            int batch, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                            float sm_scale, int pages_per_split, int num_splits,
+                            const void* new_k, const void* new_v,
+                            float* out, hipStream_t stream);
 
 /*
  * fp8_paged_decode_attn -- the same decode step over a per-tensor-scaled FP8 E4M3 cache (the

@@ -16,7 +16,7 @@ import workloads
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvkv.h")
 
-OK, INVAL, UNSUP, LAUNCH, WS = 0, -1, -2, -3, -4
+OK, INVAL, UNSUP, LAUNCH, WS, SCRATCH = 0, -1, -2, -3, -4, -5
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,7 @@ def _declared():
 
 def test_every_declared_function_is_exported_and_bound(lib):
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib._lib, n), f"{n} not exported by libnvkv.so"
         assert n in lib.EXPORTED, f"{n} has no binding"
@@ -45,7 +45,7 @@ def test_header_is_plain_c():
 
 
 def test_status_strings(lib):
-    for st in (OK, INVAL, UNSUP, LAUNCH, WS, 12345):
+    for st in (OK, INVAL, UNSUP, LAUNCH, WS, SCRATCH, 12345):
         assert isinstance(lib.status_string(st), str) and lib.status_string(st)
     assert lib.version() >= 100
 
@@ -133,6 +133,30 @@ def test_timed_decode_validates_like_the_plain_call(lib, kw, want):
                                                 a["page"], a["sm"], a["pps"], a["ns"], a["nk"], a["nv"], a["out"],
                                                 a["ws"], a["wsb"], S, None, None)
     assert st == want
+
+
+def _decode_noalloc(lib, **kw):
+    a = dict(q=A, kd=A, ks=A, vd=A, vs=A, gk=1.0, gv=1.0, pt=A, maxp=4, sl=A, b=1, hq=8, hkv=2, d=128, page=16,
+             sm=0.1, pps=2, ns=4, nk=None, nv=None, out=A)
+    a.update(kw)
+    return lib._lib.nvfp4_paged_decode_attn_noalloc(a["q"], a["kd"], a["ks"], a["vd"], a["vs"], a["gk"], a["gv"],
+                                                    a["pt"], a["maxp"], a["sl"], a["b"], a["hq"], a["hkv"], a["d"],
+                                                    a["page"], a["sm"], a["pps"], a["ns"], a["nk"], a["nv"], a["out"],
+                                                    S)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), INVAL), (dict(kd=None), INVAL), (dict(out=MIS), INVAL), (dict(d=64), UNSUP),
+    (dict(hq=64, hkv=2), UNSUP), (dict(gk=float("inf")), INVAL), (dict(sm=0.0), INVAL), (dict(ns=0), INVAL),
+    (dict(nk=A), INVAL),
+    # partials beyond the library-held array: 64 x 64 rows x 16 splits x 520 B = 34,078,720 B > 32 MiB
+    (dict(b=64, hq=64, hkv=8, ns=16), SCRATCH),
+    (dict(b=64, hq=64, hkv=8, ns=16, q=None), INVAL),       # argument errors are reported first
+])
+def test_noalloc_decode_validation(lib, kw, want):
+    assert lib.decode_noalloc_max_bytes() == 32 << 20
+    assert lib.decode_workspace_size(64, 64, 8, 15) <= 32 << 20 < lib.decode_workspace_size(64, 64, 8, 16)
+    assert _decode_noalloc(lib, **kw) == want
 
 
 def test_fp8_decode_and_layers_validation(lib):
