@@ -504,7 +504,7 @@ def precision_studies(nv, workloads, dev):
     x 8192 tokens, the stack's per-layer channel scales and outlier channels), and the per-tensor
     scale variants on one layer; prints one JSON line."""
     import torch
-    from bit_paged_kv_amd import analysis
+    import studies as analysis
     base = workloads.config(4)
     wl = workloads.Workload(name="sweep", seed=base.seed, batch=4, h_kv=base.h_kv, h_q=base.h_q,
                             seq_lens=[8192] * 4, chan=base.chan, layers=base.layers, fp8_layers=base.fp8_layers)

@@ -1,4 +1,7 @@
-"""Precision studies built from the library's own calls.
+"""Precision studies built from the library's own calls (run by ``bench.py --config sweep``).
+
+Not part of the library: the studies need a reference attention on the unquantized K/V, which
+lives here, beside the bench, rather than in the binding package.
 
 * layer_sensitivity -- the per-layer sweep behind the mixed-precision rule of [O] "03 Mixed-precision
   KV Cache" (sensitive layers keep FP8): for every layer, the decode output with the layer's cache in
@@ -16,7 +19,7 @@ from __future__ import annotations
 
 import torch
 
-from . import _lib, paged
+from bit_paged_kv_amd import _lib, paged
 
 
 def attention_reference(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens, sm_scale: float) -> torch.Tensor:

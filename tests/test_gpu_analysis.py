@@ -1,4 +1,4 @@
-"""GPU checks of the precision studies (bit_paged_kv_amd.analysis): the per-layer sensitivity sweep
+"""GPU checks of the precision studies (studies.py, beside the bench): the per-layer sensitivity sweep
 and the per-tensor scale variants, on constructed data whose answer is known."""
 import numpy as np
 import pytest
@@ -13,8 +13,8 @@ DEV = "cuda:0"
 
 @pytest.fixture(scope="module")
 def an():
-    from bit_paged_kv_amd import analysis
-    return analysis
+    import studies
+    return studies
 
 
 def _bf16(a):
