@@ -101,6 +101,17 @@ int nvfp4_pool_status(const uint8_t* k_data, const uint8_t* k_scale, const uint8
 
 }  // namespace
 
+namespace nvkv {
+
+// Split partials of a multi-split decode: per (query row, split) 128 unnormalised output floats,
+// then per (query row, split) the (max, sum) pair -- the layout the decode kernels use.
+size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits) {
+  (void)hkv;
+  return num_splits > 1 ? (size_t)batch * hq * num_splits * (kD + 2) * sizeof(float) : 0;
+}
+
+}  // namespace nvkv
+
 extern "C" {
 
 const char* nvkv_status_string(int status) {
@@ -173,7 +184,7 @@ int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long tot
   if (batch < 1 || num_kv_heads < 1 || max_seq_len < 1 || total_tokens < 0 || force_pages_per_split < 0 ||
       !pages_per_split || !num_splits)
     return NVKV_E_INVAL;
-  const long long max_pages = (max_seq_len + kPage - 1) / kPage;
+  const long long max_pages = ((long long)max_seq_len + kPage - 1) / kPage;
   long long pps = 0;
   if (force_pages_per_split > 0) {
     pps = force_pages_per_split;

@@ -651,11 +651,6 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restri
   *reinterpret_cast<f4*>(out + row * kHeadDim + d) = aa * (1.0f / dd);
 }
 
-size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits) {
-  (void)hkv;
-  return num_splits > 1 ? (size_t)batch * hq * num_splits * (kHeadDim + 2) * sizeof(float) : 0;
-}
-
 // Library-held split partials for callers that cannot allocate: one array per device, reached by
 // the kernels only through the device address hipGetSymbolAddress returns (the array's name is a
 // host-side stand-in in this code).  The partials are written before they are read, so the array
