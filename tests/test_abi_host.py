@@ -68,7 +68,7 @@ def test_plan_shapes(lib):
     assert lib.plan_decode(32, 8, 4096, 32 * 4096) == (128, 2)         # 256 streams x 2 = 512
     assert lib.plan_decode(44, 8, 8192, 44 * 8192) == (240, 3)         # 352 streams: ~3 per CU
     rag = workloads.config(3)                                          # ragged: ~4.5 per CU
-    assert lib.plan_decode(rag.batch, rag.h_kv, int(rag.total_lens.max()), int(rag.total_lens.sum())) == (216, 10)
+    assert lib.plan_decode(rag.batch, rag.h_kv, int(rag.total_lens.max()), int(rag.total_lens.sum())) == (224, 10)
     assert lib.plan_decode(1, 1, 256, 256) == (8, 2)                   # short: splits stay >= 8 pages
 
 

@@ -4,10 +4,11 @@ Shared by the tests (both the oracle side and the GPU side), ``__graft_entry__.s
 ``bench.py``.  This module only draws random numbers, rounds them to bf16 (torch's cast) and
 builds page tables; it holds none of the method's arithmetic.
 
-Every random stream is an SFC64 generator keyed by (seed, tag, layer, sequence, 8192-token chunk)
-through numpy's SeedSequence, so any one sequence can be regenerated on its own (the oracle checks
-sampled outputs of the largest workloads without generating the rest) and chunks are drawn in
-parallel threads.
+Every random stream but one is an SFC64 generator keyed by (seed, tag, layer, sequence, 8192-token
+chunk) through numpy's SeedSequence, so any one sequence of any layer can be regenerated on its own
+(the oracle checks sampled outputs of the largest workloads without generating the rest) and chunks
+are drawn in parallel threads.  The ragged lengths are the first draw of numpy's default generator
+seeded with the workload's seed.
 
 Workload recipes (the pages measure end-to-end serving of real models, which is not available;
 these synthetic shapes stand in for it):
@@ -15,10 +16,10 @@ these synthetic shapes stand in for it):
   batch32   32 x 4096, 8/32 heads, pages permuted in a shared 8192-page pool; K/V ~ N(0,1) times a
             per-(head, channel) scale log-uniform in [0.1, 10] (separate for K and V).
   long      4 x 131072, 8/64 heads, random page table; same K/V distribution.
-  ragged    64 sequences, lengths rint(exp(U(ln 512, ln 32768))), 8/64 heads, permuted pages,
-            one appended bf16 token per sequence (same distribution).
-  mixed     28 layers (FP8 at 0, 25, 26, 27), 44 x 8192, 8/32 heads; per layer K/V ~ N(0,1) with
-            2 outlier channels x20 per head; extend: a 16384-token prefix + a 2048-token chunk.
+  ragged    64 sequences, lengths clip(rint(exp(U(ln 512, ln 32768))), 512, 32768) (seed 1004: total
+            512,723), 8/64 heads, permuted pages, one appended bf16 token per sequence (same distribution).
+  mixed     28 layers (FP8 at 0, 25, 26, 27), 44 x 8192, 8/32 heads; per layer K/V ~ N(0,1) (drawn
+            per layer) with 2 outlier channels x20 per head; extend: a 16384-token prefix + a 2048-token chunk.
 q ~ N(0,1) everywhere.  softmax scale 1/sqrt(128).
 """
 from __future__ import annotations
@@ -124,14 +125,14 @@ class Workload:
             s[h, r.choice(HEAD_DIM, size=2, replace=False)] = 20.0
         return s
 
-    def kv_base(self, which: str, b: int, length: int | None = None) -> np.ndarray:
-        """fp32 [L_b][H_kv][128] standard normals of sequence b, shared by all layers."""
+    def kv_base(self, which: str, b: int, length: int | None = None, layer: int = 0) -> np.ndarray:
+        """fp32 [L_b][H_kv][128] standard normals of sequence b in layer `layer` (each layer draws its own)."""
         n = int(self.seq_lens[b]) if length is None else length
         out = np.empty((n, self.h_kv, HEAD_DIM), dtype=np.float32)
 
         def fill(c):
             lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
-            _rng(self.seed, which, 0, b, c).standard_normal(out=out[lo:hi], dtype=np.float32)
+            _rng(self.seed, which, layer, b, c).standard_normal(out=out[lo:hi], dtype=np.float32)
 
         nchunks = (n + CHUNK - 1) // CHUNK
         if nchunks == 1:
@@ -144,7 +145,7 @@ class Workload:
     def kv(self, which: str, b: int, layer: int = 0, length: int | None = None) -> torch.Tensor:
         """bf16 [L_b][H_kv][128] cached K ('k') or V ('v') of sequence b, layer `layer` (CPU tensor):
         bf16(fp32(base normal * channel scale of the layer))."""
-        x = self.kv_base(which, b, length)
+        x = self.kv_base(which, b, length, layer)
         x *= self.channel_scale(which, layer)[None]
         return to_bf16(x)
 
@@ -174,7 +175,9 @@ class Workload:
 
 
 def ragged_lengths(seed: int, batch: int, lo: int = 512, hi: int = 32768) -> np.ndarray:
-    r = _rng(seed, "lens")
+    """Log-uniform lengths: the first draw of numpy's default generator seeded with `seed`
+    (seed 1004, 64 sequences: total 512,723 tokens, from 514 to 32,330)."""
+    r = np.random.default_rng(seed)
     return np.clip(np.rint(np.exp(r.uniform(math.log(lo), math.log(hi), size=batch))), lo, hi).astype(np.int64)
 
 
