@@ -5,25 +5,28 @@
                     [--config long|batch32|ragged|mixed|extend|prefill|write|gather|tiny|sweep]
 
 One step is one decode step of the workload's hot path, inputs already resident in HBM:
-  long     split-K NVFP4 decode + log-sum-exp merge, 4 x 131072 tokens, 8 KV / 64 query heads (default)
+  long     split-K NVFP4 decode + log-sum-exp merge, 4 x 131072 tokens, 8 KV / 64 query heads (default);
+           two cache copies (1.2 GB) rotate, so no step reads a cache the previous step read
   batch32  same path, 32 x 4096 tokens, 8 / 32 heads; three cache copies rotate so that every
            step reads a cache not touched by the previous two (the 256 MB last-level cache holds one)
-  ragged   64 ragged sequences, fused quantize-append of one token per sequence + decode
+  ragged   64 ragged sequences, fused quantize-append of one token per sequence + decode (two
+           cache copies rotate)
   mixed    28 layers, FP8 at layers 0, 25, 26, 27 and NVFP4 elsewhere, 44 x 8192 tokens
   extend   per NVFP4 layer of the mixed stack: 16384-token prefix -> FP8 workspace + 2048-token
            chunk quantize-append (24 layers per step)
   prefill  per NVFP4 layer: one-pass NVFP4 cache + FP8 copy write of a prompt and causal attention
            over the copy
-  write    quantize-on-write of the ragged batch's whole cache (495,439 tokens x 8 kv heads, bf16 K
+  write    quantize-on-write of the ragged batch's whole cache (512,723 tokens x 8 kv heads, bf16 K
            and V) into a fresh NVFP4 pool; the per-tensor scale reduction is timed apart
   gather   the extend path's prefix gather alone: one NVFP4 layer's 16384-token prefix -> FP8 workspace
   tiny     1 x 256 tokens (latency-bound)
   sweep    precision studies (per-layer NVFP4 vs FP8 sensitivity, per-tensor scale variants)
 
-The timed region is exactly K steps between two device synchronisations.  The decode kernel's own
-duration comes from HIP events that its dispatch records on every 5th timed step (a recorded
-dispatch adds a few microseconds to its step); extend and prefill time each attention launch with
-events on the launch stream.  Effective KV GB/s =
+The timed region is exactly K steps between two device synchronisations, with nothing else in it.
+Right after it, the dominant kernel is timed on its own: for decode, 40 more steps whose split
+kernel's dispatch records a HIP event pair (the long workload rotates two cache copies, batch32
+three); for extend and prefill, the attention launches of two more steps between events on the
+launch stream.  Effective KV GB/s =
 NVFP4 (or FP8) bytes the step must read (144 B per token and KV head; 256 B for FP8) / step time.
 The CPU baseline times the fp64 oracle (one thread per worker) on a bounded sample of the same
 workload: dequantize + attention for the decode configs and the mixed stack (each layer in its
@@ -61,6 +64,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000     # hipEventDisableSystemFence (hip_runtime_api.h)
+
+
 class HipEventPairs:
     """K pairs of raw hipEvent_t from the HIP runtime the library runs on (timing plumbing only)."""
 
@@ -70,9 +76,17 @@ class HipEventPairs:
         self.hip = ctypes.CDLL("libamdhip64.so.7")       # the runtime torch has already loaded
         self.start = [ctypes.c_void_p() for _ in range(n)]
         self.stop = [ctypes.c_void_p() for _ in range(n)]
+        # timing-only events: no system-scope fence (cache writeback and invalidation) when they are
+        # recorded, which would otherwise lengthen the bracketed kernel and the work after it
         for e in self.start + self.stop:
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(HIP_EVENT_DISABLE_SYSTEM_FENCE)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, i, which, stream):
+        """hipEventRecord of start (which == 0) or stop event i on the raw stream handle."""
+        ev = (self.start if which == 0 else self.stop)[i]
+        if self.hip.hipEventRecord(ev, self._ct.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self):
         ms = self._ct.c_float()
@@ -88,16 +102,39 @@ class HipEventPairs:
             self.hip.hipEventDestroy(e)
 
 
-EVENT_EVERY = 5     # decode configs: timed steps per dispatch-recorded kernel duration
+KERNEL_SAMPLES = 40    # decode configs: launches timed one by one after the headline loop
 
-# HBM traffic of decode_split_kernel on the long workload, from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-# (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives (x2.000 / x1.000).  Valid only
-# for the kernel sources (the decode file and the headers it includes, hashed together) and the
-# split plan they were taken with; reported as null otherwise.
+# Worker processes of the CPU baseline: one per core of the process's affinity set, at most 16 --
+# the host-CPU share one GPU gets on the machines the benchmark runs on (a pool wider than that
+# share would be time-sliced, not faster).
+CPU_WORKER_CAP = 16
+
+
+def host_cpu():
+    """CPU model (from /proc/cpuinfo), cores in the affinity set, and the worker count used."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0))
+    return {"model": model, "affinity_cores": avail, "workers": max(1, min(avail, CPU_WORKER_CAP)),
+            "worker_cap": CPU_WORKER_CAP,
+            "cap_reason": "one spawned worker per affinity core, at most 16: the host-CPU share of one GPU"}
+
+# HBM traffic of one decode step (decode_split_kernel + merge_splits_kernel) on the long workload, from
+# rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch, one counter per run) scaled by
+# the factors a plain 1 GiB device copy gives (x2.000 / x1.000).  Valid only for the kernel sources
+# (the decode file and the headers it includes, hashed together) and the split plan they were taken
+# with; reported as null otherwise.
 TRAFFIC = {
-    "long": {"source_sha256": "f69eb3d6530819662c03d1604cb0db9a00ef6e95cc9bffe2b8be9d511e19b638",
-             "plan": [512, 16], "fetch_kib": 296023.6, "write_kib": 2208.1, "fetch_factor": 2.0,
-             "write_factor": 1.0},
+    "long": {"source_sha256": "1e4675a0642f3f7ff8a90d4104802a32bfa8adc858865d2e02cb41fadd9019e7", "plan": [512, 16],
+             "kernels": {"decode_split_kernel": (296026.5, 2203.1), "merge_splits_kernel": (1063.0, 128.0)},
+             "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
 
@@ -194,7 +231,7 @@ def cpu_baseline(cfg_index, budget_s=6.0):
 
     import workloads
     wl = workloads.config(cfg_index)
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16, wl.batch * wl.h_kv))
+    cores = max(1, min(host_cpu()["workers"], wl.batch * wl.h_kv))
     all_units = [(b, hk) for b in range(wl.batch) for hk in range(wl.h_kv)]
     jobs = []
     n = len(all_units)
@@ -213,7 +250,7 @@ def cpu_baseline(cfg_index, budget_s=6.0):
             "sample": f"{total} KV bytes of (sequence, kv head) units of {int(wl.seq_lens.min())}..{int(wl.seq_lens.max())}-token sequences "
                       f"(fp64 dequantize + softmax attention for {wl.group} query heads each), {spent:.1f} s of oracle "
                       f"time over {cores} single-threaded workers; rate summed over workers; host "
-                      f"{platform.processor() or platform.machine()}"}
+                      f"{host_cpu()['model']}", "host": host_cpu()}
 
 
 def _cpu_mixed_units(args):
@@ -377,7 +414,7 @@ def cpu_baseline_write(cfg_index, budget_s=6.0):
 
     import workloads
     wl = workloads.config(cfg_index)
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cores = host_cpu()["workers"]
     # units spread over the batch so that every worker sees long and short sequences
     all_units = [(b, hk) for hk in range(wl.h_kv) for b in range(wl.batch)]
     jobs = []
@@ -395,7 +432,7 @@ def cpu_baseline_write(cfg_index, budget_s=6.0):
             "sample": f"{total} bytes (bf16 K+V read, NVFP4 written) of (sequence, kv head) units of the ragged "
                       f"cache (fp32 NVFP4 block quantizer of K and V; scales of the unit's sequence), {spent:.1f} s of "
                       f"oracle time over {cores} single-threaded workers; rate summed over workers; host "
-                      f"{platform.processor() or platform.machine()}"}
+                      f"{host_cpu()['model']}", "host": host_cpu()}
 
 
 def _cpu_gather_units(args):
@@ -438,7 +475,7 @@ def cpu_baseline_gather(cfg_index, budget_s=6.0):
 
     import workloads
     wl = workloads.config(cfg_index)
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cores = host_cpu()["workers"]
     all_units = [(layer, hk) for layer in range(wl.layers) if not wl.is_fp8(layer) for hk in range(wl.h_kv)]
     n = len(all_units)
     jobs = [(cfg_index, all_units[w * n // cores:(w + 1) * n // cores], budget_s) for w in range(cores)]
@@ -450,7 +487,7 @@ def cpu_baseline_gather(cfg_index, budget_s=6.0):
     return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{total} bytes (NVFP4 read, FP8 written) of (layer, kv head) units of the 16384-token extend "
                       f"prefix (fp32 transcode of K and V), {spent:.1f} s of oracle time over {cores} single-threaded "
-                      f"workers; rate summed over workers; host {platform.processor() or platform.machine()}"}
+                      f"workers; rate summed over workers; host {host_cpu()['model']}", "host": host_cpu()}
 
 
 def cpu_baseline_stack(cfg_index, mode, budget_s=6.0, rows=1024):
@@ -461,7 +498,7 @@ def cpu_baseline_stack(cfg_index, mode, budget_s=6.0, rows=1024):
 
     import workloads
     wl = workloads.config(cfg_index)
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cores = host_cpu()["workers"]
     if mode == "mixed":
         all_units = [(layer, b) for b in range(wl.batch) for layer in range(wl.layers)]
     else:
@@ -473,7 +510,7 @@ def cpu_baseline_stack(cfg_index, mode, budget_s=6.0, rows=1024):
         jobs.append((cfg_index, mine, budget_s) if mode == "mixed" else (cfg_index, mode, mine, budget_s, rows))
     with mp.get_context("spawn").Pool(cores) as pool:
         res = pool.map(_cpu_mixed_units if mode == "mixed" else _cpu_extend_units, jobs)
-    host = platform.processor() or platform.machine()
+    host = host_cpu()["model"]
     if mode == "mixed":
         total = sum(r[0] for r in res)
         rate = sum(r[0] / r[1] for r in res if r[1] > 0)
@@ -482,7 +519,7 @@ def cpu_baseline_stack(cfg_index, mode, budget_s=6.0, rows=1024):
                 "sample": f"{total} KV bytes of (layer, sequence) units taken in layer order per sequence (each "
                           f"layer in its own precision, FP8 scales of the unit's sequence; fp64 dequantize + "
                           f"softmax attention over 8 kv heads), {spent:.1f} s of oracle time over {cores} "
-                          f"single-threaded workers; rate summed over workers; host {host}"}
+                          f"single-threaded workers; rate summed over workers; host {host}", "host": host_cpu()}
     total = sum(r[0] for r in res)
     rate = sum(r[0] / r[1] for r in res if r[1] > 0)
     tflops = sum(r[2] / r[1] for r in res if r[1] > 0) / 1e12
@@ -495,7 +532,8 @@ def cpu_baseline_stack(cfg_index, mode, budget_s=6.0, rows=1024):
     return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "attention_tflops": round(tflops, 6),
             "sample": f"{total} step bytes of (layer, kv head) units ({what}; fp64), {spent:.1f} s of oracle "
-                      f"time over {cores} single-threaded workers; rate summed over workers; host {host}"}
+                      f"time over {cores} single-threaded workers; rate summed over workers; host {host}",
+            "host": host_cpu()}
 
 
 # ------------------------------------------------------------------------------------------------
@@ -559,7 +597,8 @@ def main():
     # ---- build the step ------------------------------------------------------------------------
     att_flops = 0            # extend: attention flops per launch
     if name in ("long", "batch32", "tiny", "ragged"):
-        copies = 3 if name in ("batch32", "tiny") else 1
+        # copies rotate so that no step reads a pool the 256 MB last-level cache may still hold
+        copies = 3 if name in ("batch32", "tiny") else 2
         pools = []
         for c in range(copies):
             pool, gk, gv = build_layer_cache(nv, wl, 0, dev)
@@ -597,7 +636,7 @@ def main():
                  "fused_append": bool(wl.append)}
         tokens_per_step = wl.batch
     elif name == "write":
-        # quantize-on-write of a whole cache: the ragged batch's 495,439 cached tokens x 8 kv heads,
+        # quantize-on-write of a whole cache: the ragged batch's 512,723 cached tokens x 8 kv heads,
         # bf16 K and V, into a fresh NVFP4 pool at the page table's slots (misaligned sequence starts);
         # the per-tensor scales are computed once beforehand, as a prefill would
         k, v, slots = (torch.cat([wl.kv("k", b) for b in range(wl.batch)]).to(dev),
@@ -714,11 +753,11 @@ def main():
             for write, attend in layer_calls:
                 write.run()
                 if events is not None:
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
+                    k = len(att_events)
+                    events.record(k, 0, stream.cuda_stream)
                     attend.run()
-                    e1.record(stream)
-                    att_events.append((e0, e1))
+                    events.record(k, 1, stream.cuda_stream)
+                    att_events.append(k)
                 else:
                     attend.run()
         # bytes of the write: read bf16 K+V (512 B per token-head), write NVFP4 (144 B) and FP8 (256 B)
@@ -777,11 +816,11 @@ def main():
                 gather.run()
                 append.run()
                 if events is not None:
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
+                    k = len(att_events)
+                    events.record(k, 0, stream.cuda_stream)
                     attend.run()
-                    e1.record(stream)
-                    att_events.append((e0, e1))
+                    events.record(k, 1, stream.cuda_stream)
+                    att_events.append(k)
                 else:
                     attend.run()
                 quantize.run()
@@ -802,26 +841,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # the split kernel's own dispatch records an event pair on every EVENT_EVERY-th timed step (no
-    # commands are added to the stream; a recorded dispatch costs the step a few microseconds, so
-    # not every step records); the step as a whole is bracketed by device synchronisations
-    events = None
-    event_every = 1
-    if timed_kernel and timed_kernel.startswith("decode_split_kernel"):
-        event_every = EVENT_EVERY
-        events = HipEventPairs((args.steps + event_every - 1) // event_every)
-    elif timed_kernel == "extend_attn_kernel":
-        events = True          # the step records torch events around each attention launch
+    # the headline region holds nothing but the K steps: no per-launch events inside it
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
-        if i % event_every == 0:
-            step(events, i // event_every)
-        else:
-            step()
+    for _ in range(args.steps):
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -829,21 +855,49 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+
+    # ---- the dominant kernel's own duration, right after the headline region ---------------------
+    split_only = None
     if timed_kernel == "extend_attn_kernel":
-        kms = [e0.elapsed_time(e1) for e0, e1 in att_events]
-        kernel_ms = sum(kms) / len(kms)
-        achieved = att_flops / (kernel_ms * 1e-3) / 1e12
-        bound, peak, unit = "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-        timing = (f"{timed_kernel}: mean of {len(kms)} launches (min {min(kms) * 1e3:.1f} us, max "
-                  f"{max(kms) * 1e3:.1f} us), torch events on the launch stream around each launch")
-    elif timed_kernel:
+        # two more steps, each attention launch between timing-only events on its launch stream
+        att_events.clear()
+        events = HipEventPairs(2 * len(layer_calls))
+        for _ in range(2):
+            step(events)
+        torch.cuda.synchronize()
         kms = events.elapsed_ms()
         events.close()
         kernel_ms = sum(kms) / len(kms)
+        achieved = att_flops / (kernel_ms * 1e-3) / 1e12
+        bound, peak, unit = "mfma", MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        timing = (f"{timed_kernel}: mean of {len(kms)} launches in 2 steps after the timed region (min "
+                  f"{min(kms) * 1e3:.1f} us, max {max(kms) * 1e3:.1f} us), timing-only HIP events (no system "
+                  f"fence) recorded on the launch stream around each launch")
+    elif timed_kernel:
+        # The decode step is two back-to-back kernels (split kernel, then the log-sum-exp merge when
+        # there are several splits).  The roofline unit is the step: its duration comes from the HIP
+        # events around the K timed steps (on the launch stream), which hold nothing else; a kernel
+        # trace of the same command shows the two kernels and the gap between them adding up to it.
+        kernel_ms = step_gpu_ms
         achieved = kernel_bytes / (kernel_ms * 1e-3) / 1e9
-        timing = (f"{timed_kernel}: mean of {len(kms)} per-launch durations (every {event_every}th of the "
-                  f"{args.steps} timed steps; min {min(kms) * 1e3:.1f} us, max {max(kms) * 1e3:.1f} us) from "
-                  f"hipEvents its dispatch recorded on the launch stream")
+        # the split kernel alone, for reference: KERNEL_SAMPLES more steps whose split-kernel dispatch
+        # records timing-only events (the recording itself adds a few microseconds inside the bracket)
+        events = HipEventPairs(KERNEL_SAMPLES)
+        for i in range(KERNEL_SAMPLES):
+            step(events, i)
+        torch.cuda.synchronize()
+        kms = events.elapsed_ms()
+        events.close()
+        srt = sorted(kms)
+        split_only = {"kernel": "decode_split_kernel<PageNv4>", "mean_us": round(sum(kms) / len(kms) * 1e3, 2),
+                      "median_us": round(srt[len(srt) // 2] * 1e3, 2), "min_us": round(srt[0] * 1e3, 2),
+                      "max_us": round(srt[-1] * 1e3, 2), "samples": len(kms),
+                      "method": "hipEvents (no system fence) recorded by the split kernel's own dispatch, in "
+                                f"{KERNEL_SAMPLES} steps after the timed region; the recording adds a few us"}
+        timed_kernel = ("decode step: decode_split_kernel<PageNv4>" +
+                        (" + merge_splits_kernel" if extra.get("num_splits", 1) > 1 else ""))
+        timing = (f"HIP events on the launch stream around the {args.steps} timed steps, divided by "
+                  f"{args.steps}: the step's kernels back to back, nothing else in the region")
     else:
         kernel_ms = step_gpu_ms
         achieved = step_bytes / (kernel_ms * 1e-3) / 1e9
@@ -899,13 +953,14 @@ def main():
 
     traffic, traffic_detail = None, None
     t = TRAFFIC.get(name)
-    if t is not None and timed_kernel.startswith("decode_split_kernel"):
+    if t is not None and timed_kernel.startswith("decode step"):
         if decode_source_sha256() == t["source_sha256"] and list(plan) == t["plan"]:
-            rd = t["fetch_kib"] * 1024 * t["fetch_factor"]
-            wr = t["write_kib"] * 1024 * t["write_factor"]
+            rd = sum(f for f, _ in t["kernels"].values()) * 1024 * t["fetch_factor"]
+            wr = sum(w for _, w in t["kernels"].values()) * 1024 * t["write_factor"]
             traffic = round(rd + wr)
             traffic_detail = {"read_bytes": round(rd), "write_bytes": round(wr),
                               "algorithmic_read_bytes": kernel_bytes,
+                              "per_kernel_kib_fetch_write": {k: list(v) for k, v in t["kernels"].items()},
                               "source": "rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE per dispatch x copy calibration"}
         else:
             traffic_detail = "kernel source or split plan changed since the counters were taken"
@@ -936,6 +991,8 @@ def main():
     }
     if gscale is not None:
         res["global_scale"] = gscale
+    if split_only is not None:
+        res["roofline"]["split_kernel_alone"] = split_only
     if ceiling is not None:
         res["stream_read_ceiling"] = ceiling
         res["pct_of_stream_read_ceiling"] = round(100.0 * value / ceiling["value"], 2)
