@@ -70,7 +70,11 @@ int decode_args_status(const void* q, const int32_t* page_table, int max_pages_p
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4)) return NVKV_E_INVAL;
   if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return NVKV_E_INVAL;
   if (pages_per_split < 1 || num_splits < 1) return NVKV_E_INVAL;
-  if ((long long)num_splits * batch * num_kv_heads > 0x7FFFFFFFLL) return NVKV_E_INVAL;   // one grid axis
+  // unit counts (pages x kv heads) and piece offsets are 32-bit in the kernels
+  if ((long long)batch * (max_pages_per_seq + nvkv::kStreamCostPages) * num_kv_heads + 2LL * num_splits >
+          0x7FFFFFFFLL ||
+      (long long)num_splits * pages_per_split > 0x7FFFFFFFLL)
+    return NVKV_E_UNSUPPORTED;
   return NVKV_OK;
 }
 
@@ -105,9 +109,11 @@ namespace nvkv {
 
 // Split partials of a multi-split decode: per (query row, split) 128 unnormalised output floats,
 // then per (query row, split) the (max, sum) pair -- the layout the decode kernels use.
+// Partial slots: one per (piece, stream) pair along the unit order, at most pieces + streams - 1.
 size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits) {
-  (void)hkv;
-  return num_splits > 1 ? (size_t)batch * hq * num_splits * (kD + 2) * sizeof(float) : 0;
+  if (num_splits <= 1) return 0;
+  const size_t slots = (size_t)num_splits + (size_t)batch * hkv;
+  return slots * (size_t)(hq / hkv) * (kD + 2) * sizeof(float);
 }
 
 }  // namespace nvkv
@@ -185,41 +191,30 @@ int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long tot
       !pages_per_split || !num_splits)
     return NVKV_E_INVAL;
   const long long max_pages = ((long long)max_seq_len + kPage - 1) / kPage;
-  long long pps = 0;
+  // the step's units (pages x kv heads): from the total when given (each sequence rounds up to
+  // whole pages), else every sequence as long as the longest
+  long long seq_pages = (long long)batch * max_pages;
+  if (total_tokens > 0) seq_pages = std::min(seq_pages, (total_tokens + (long long)batch * (kPage - 1)) / kPage);
+  const long long units = std::max(1LL, seq_pages * num_kv_heads);
+  long long pps, pieces;
   if (force_pages_per_split > 0) {
-    pps = force_pages_per_split;
+    // pieces of the forced size, rounded up to even (whole pairs of pages) and at most the step
+    pps = std::min<long long>((force_pages_per_split + 1LL) & ~1LL, std::max(2LL, (units + 1) & ~1LL));
+    pieces = (units + pps - 1) / pps;
   } else {
-    const long long cus = device_cus();
-    const long long streams = (long long)batch * num_kv_heads;
-    // ragged batch (lengths known to differ from the longest)
-    const bool ragged = total_tokens > 0 && total_tokens * 10 < (long long)batch * max_seq_len * 9;
-    // Equal lengths and a stream count that divides two workgroups per compute unit: exactly two
-    // per unit, the fastest shape measured (long contexts, 32 streams x 16 splits: 116-118 us
-    // against 119-120 us at three per unit; 32 x 4096, 256 streams x 2: 34.5 against 36 us),
-    // while splits stay at least 64 pages long.
-    if (!ragged && (2 * cus) % streams == 0) {
-      const long long splits2 = 2 * cus / streams;
-      const long long p2 = (((max_pages + splits2 - 1) / splits2) + 7) & ~7LL;
-      if (p2 >= 64) pps = p2;
-    }
-    if (pps == 0) {
-      // otherwise the page-heads of the step spread over ~3 workgroups per unit (the kernel's
-      // occupancy; an uneven 2.75 per unit measured slower), or 4.5 for a ragged batch, so that
-      // the hardware can hand the splits of short sequences to units that finished early
-      const long long seq_pages = total_tokens > 0 ? (total_tokens + (long long)batch * (kPage - 1)) / kPage
-                                                   : (long long)batch * max_pages;
-      const long long work = seq_pages * num_kv_heads;
-      const long long target = ragged ? cus * 9 / 2 : cus * 3;
-      pps = std::max<long long>(8, (work + target - 1) / target);
-      pps = (pps + 7) & ~7LL;                           // whole pairs of pages for each of the 4 waves
-    }
+    // Two workgroups per compute unit, each with an equal piece of the step, all resident at once:
+    // on equal lengths this is the fastest shape measured (long contexts: 16 pieces per stream,
+    // 116-118 us against 119-120 us at three per unit; 32 x 4096: 34.5 against 36 us), and on a
+    // ragged batch it leaves no workgroup waiting for a slot and no tail of short splits.  Small
+    // steps keep pieces of at least kMinPiecePages pages.
+    constexpr long long kMinPiecePages = 16;
+    pps = 2;
+    pieces = std::min<long long>(2 * device_cus(), (units + kMinPiecePages - 1) / kMinPiecePages);
   }
-  pps = (pps + 1) & ~1LL;
-  pps = std::min<long long>(pps, std::max<long long>(2, (max_pages + 1) & ~1LL));
-  const long long splits = (max_pages + pps - 1) / pps;
-  if (splits > 0x7FFFFFFFLL) return NVKV_E_UNSUPPORTED;
+  pieces = std::max(1LL, pieces);
+  if (pieces > 0x3FFFFFFFLL || pieces * pps > 0x7FFFFFFFLL) return NVKV_E_UNSUPPORTED;
   *pages_per_split = (int)pps;
-  *num_splits = (int)std::max<long long>(1, splits);
+  *num_splits = (int)pieces;
   return NVKV_OK;
 }
 

@@ -263,15 +263,53 @@ __device__ __forceinline__ void issue_priority(int left, int total) {
     __builtin_amdgcn_s_setprio(0);
 }
 
-// Splits that a sequence of n_pages pages uses under the plan (pages_per_split, num_splits).
-__device__ __forceinline__ int seq_splits(int n_pages, int pages_per_split, int num_splits) {
-  return min(num_splits, max(1, (n_pages + pages_per_split - 1) / pages_per_split));
+// Pages of a sequence of `len` tokens (lengths are >= 1).
+__device__ __forceinline__ int seq_pages(int len) { return (len + kPageSize - 1) / kPageSize; }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v = min(v, __shfl_xor(v, d, 64));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v = max(v, __shfl_xor(v, d, 64));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+// Sum across the 64 lanes of a wave, returned as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
-// Workspace of a multi-split decode: per (row = b * Hq + h, split) the unnormalised partial output
-// [128] (times g_V), then per (row, split) its (max, sum) in log2 units.  Every entry is written
-// before it is read, so the workspace needs no initialisation.
-// One workgroup of four waves per (sequence, kv head, split).
+// The step's work is the sequence of units of the streams s = b * Hkv + h in order; stream s owns
+// pages(b) + extra units, extra = kStreamCostPages when the lengths differ (else 0): virtual units
+// at its start that stand for the fixed cost of starting a segment (the page-id and first page
+// round trips, the combine), followed by one unit per page.  The units are cut into `pieces`
+// consecutive pieces of piece_pages(...) units, an even count of at least min_pages, and
+// workgroup i takes piece i: every workgroup of a grid that fits the GPU at once then has about
+// the same cost, whatever the length mix (a piece that holds many short streams gets fewer pages).
+__device__ __forceinline__ int piece_pages(int total_units, int pieces, int min_pages) {
+  return max(min_pages, (((total_units + pieces - 1) / pieces) + 1) & ~1);
+}
+
+// One workgroup of four waves per piece.  A piece is walked as segments (the pages of one stream
+// it holds); each wave takes a contiguous, even-sized quarter of a segment and the four combine in
+// LDS.  A segment holding a whole stream writes the normalised output; the others write their
+// unnormalised partial output (times g_V) and (max, sum) in log2 units at partial slot
+// (piece + stream) -- unique, since both grow along the unit order -- for the merge kernel.
+// Workspace: partial outputs [num_splits + B * Hkv][group][128], then (max, sum) pairs
+// [num_splits + B * Hkv][group]; every entry read is written first, so it needs no initialisation.
 //
 // kPack (query heads per kv head <= 8): score columns 8..15 repeat heads 0..7, and those lanes feed
 // the low fp16 part of P into the PV product while columns 0..7 feed the high part, so one MFMA per
@@ -280,335 +318,378 @@ template <typename Page, bool kPack>
 __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Workgroup order: split-major with the stream index rotated by the split, so that the splits of
-  // a (sequence, kv head) stream are spread over the dispatch order and over the XCDs.
-  const int n_streams = a.batch * a.hkv;
-  const int split = (int)(blockIdx.x / (unsigned)n_streams);
-  const int stream = (int)((blockIdx.x - (unsigned)split * n_streams + (unsigned)(n_streams - split % n_streams)) %
-                           (unsigned)n_streams);
-  const int b = stream / a.hkv, hk = stream - b * a.hkv;
   const int group = a.hq / a.hkv;
-  const int seq_len = a.seq_lens[b];
-  const int n_pages = (seq_len + kPageSize - 1) / kPageSize;
-  // This sequence needs ceil(pages / pages_per_split) splits (at least one, at most num_splits),
-  // the last of them taking the remainder; the grid's other splits of the stream exit here and
-  // write nothing (the merge reads only the splits a sequence has).
-  const int n_split_b = seq_splits(n_pages, a.pages_per_split, a.num_splits);
-  if (split >= n_split_b) return;
-  const int wg_begin = split * a.pages_per_split;
-  const int wg_end = (split == n_split_b - 1) ? n_pages : wg_begin + a.pages_per_split;
-  // each wave takes a contiguous, even-sized quarter of them
-  const int quarter = (((wg_end - wg_begin + kWaves - 1) / kWaves) + 1) & ~1;
-  const int pg_begin = min(wg_end, wg_begin + wave * quarter);
-  const int pg_end = min(wg_end, pg_begin + quarter);
-  const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
-  const int col = lane & 15, c = lane >> 4;
-  const int jh = kPack ? (col & 7) : col;          // query head (within the group) of this lane's column
-  const bool lo_lane = kPack && col >= 8;          // packed: this column carries the low part of P
+
+  // ---- this workgroup's piece: lanes hold the lengths of sequences base .. base + 63 ----
+  int len_l = 0, incl_l = 0, total = 0, lmin = 0x7FFFFFFF, lmax = 0;
+  for (int base = 0; base < a.batch; base += 64) {
+    const bool ok = base + lane < a.batch;
+    len_l = ok ? a.seq_lens[base + lane] : 0;
+    lmin = min(lmin, wave_min(ok ? len_l : 0x7FFFFFFF));
+    lmax = max(lmax, wave_max(len_l));
+    incl_l = wave_incl_scan(ok ? seq_pages(len_l) : 0, lane);
+    total += __builtin_amdgcn_readlane(incl_l, 63);   // readlane: a wave-uniform (scalar) value
+  }
+  const int extra = lmin == lmax ? 0 : kStreamCostPages;
+  const int units = (total + extra * a.batch) * a.hkv;
+  const int pp = piece_pages(units, (int)gridDim.x, a.pages_per_split);
+  int u0 = (int)blockIdx.x * pp;
+  if (u0 >= units) return;
+  const int u1 = min(units, u0 + pp);
+  // the sequence holding unit u0: the first with Hkv * (cost up to and including it) > u0
+  int base = 0, before = 0;   // before: cost of the sequences before `base`
+  if (a.batch > 64) {
+    for (;; base += 64) {
+      len_l = base + lane < a.batch ? a.seq_lens[base + lane] : 0;
+      incl_l = wave_incl_scan(base + lane < a.batch ? seq_pages(len_l) : 0, lane);
+      const int chunk = __builtin_amdgcn_readlane(incl_l, 63) + extra * min(64, a.batch - base);
+      if ((before + chunk) * a.hkv > u0) break;
+      before += chunk;
+    }
+  }
+  const int cost_l = incl_l + extra * (lane + 1);   // cost of sequences base .. base + lane
+  const unsigned long long hit = __ballot(base + lane < a.batch && (before + cost_l) * a.hkv > u0);
+  const int lb = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+  int b = base + lb;
+  int seq_len = __builtin_amdgcn_readlane(len_l, lb);
+  int n_pages = seq_pages(seq_len);
+  const int seq_start = (before + __builtin_amdgcn_readlane(cost_l, lb) - n_pages - extra) * a.hkv;   // first unit of b
+  int hk = (u0 - seq_start) / (n_pages + extra);
+  int s_start = seq_start + hk * (n_pages + extra);                                                 // of stream (b, hk)
+
   __shared__ uint32_t vs_lds[kWaves][128];                  // per-wave exchange slot for V scale pairs
   __shared__ float red_o[kWaves][16][kHeadDim];             // per-wave partial outputs
   __shared__ float red_ml[kWaves][16][2];                   // per-wave (max, sum) per query head
-  uint32_t* vs_slot = vs_lds[wave];
-  const bool head_ok = jh < group;
-  const int hq = hk * group + (head_ok ? jh : 0);
-  const size_t row = (size_t)b * a.hq + hq;
 
-  if constexpr (std::is_same<Page, PageNv4>::value) {
-    if (a.new_k != nullptr) {
-      const int pos = seq_len - 1;
-      if (pos / kPageSize >= pg_begin && pos / kPageSize < pg_end) {
-        append_token_nvfp4(a, b, hk, pos, pt[pos / kPageSize], lane);
-        // only this wave reads the page back; its stores reach L2 (L1 writes through, and L1 holds no
-        // copy of the page: it is invalidated at kernel start), so waiting for them suffices
-        __threadfence_block();
-      }
-    }
-  }
+  for (;;) {
+    // the length of the sequence after b, read ahead (scalar) for the step to the next stream
+    const int next_len = b + 1 < a.batch ? a.seq_lens[b + 1] : 0;
+    // segment: pages [seg_begin, seg_end) of stream (b, hk), whose pages are units r0 .. r0 + n_pages
+    const int r0 = s_start + extra;
+    const int seg_begin = max(u0, r0) - r0, seg_end = min(u1 - r0, n_pages);
+    const bool has_pages = seg_begin < seg_end;   // a piece may end inside the virtual units
+    if (has_pages) {
+      // lane-derived values are recomputed for every segment (the lane index is opaque to the
+      // compiler), so that none of them is hoisted and kept in a register across the whole piece
+      const int lane = opaque_lane_id();
+      const int col = lane & 15, c = lane >> 4;
+      const int jh = kPack ? (col & 7) : col;          // query head (within the group) of this lane's column
+      const bool lo_lane = kPack && col >= 8;          // packed: this column carries the low part of P
+      uint32_t* vs_slot = vs_lds[wave];
+      const bool head_ok = jh < group;
+      const bool whole = seg_begin == 0 && seg_end == n_pages;
+      // each wave takes a contiguous, even-sized quarter of the segment
+      const int quarter = (((seg_end - seg_begin + kWaves - 1) / kWaves) + 1) & ~1;
+      const int pg_begin = min(seg_end, seg_begin + wave * quarter);
+      const int pg_end = min(seg_end, pg_begin + quarter);
+      const int32_t* pt = a.page_table + (size_t)b * a.max_pages;
+      const int hq = hk * group + (head_ok ? jh : 0);
+      const size_t row = (size_t)b * a.hq + hq;
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  f4 o[8];
-#pragma unroll
-  for (int n = 0; n < 8; ++n) o[n] = f4{0.f, 0.f, 0.f, 0.f};
-
-  if (pg_begin < pg_end) {
-    // q row -> fp16 B operands, rescaled by a power of two so the row maximum sits in [2^13, 2^14).
-    // The raw row is loaded with the first page ids (every lane reads a valid row: absent heads
-    // read head 0 and zero it), and converted while the first pages are in flight, so the wave
-    // waits for two memory round trips before its first scores, not three.
-    h8 qb[4];
-    float qk_scale = 0.0f;
-    uint4 q_raw[4];
-    auto load_q = [&] {
-      const uint4* qp =
-          reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + row * kHeadDim + 32 * c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q_raw[i] = qp[i];
-    };
-    auto prep_q = [&] {
-      float qf[32];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bf16x8_to_f32(q_raw[i], qf + 8 * i);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) qf[i] = head_ok ? qf[i] : 0.0f;
-      float qmax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qf[i]));
-      qmax = max_xor16(qmax);
-      qmax = max_xor32(qmax);
-      int qexp = 0;
-      if (qmax > 0.0f) {
-        int ex;
-        (void)frexpf(qmax, &ex);          // qmax = f * 2^ex, f in [0.5, 1)
-        qexp = min(max(14 - ex, -100), 100);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qb[s][i] = (_Float16)__builtin_ldexpf(qf[8 * s + i], qexp);
-      // scores in log2 units: <q, K_hat> * sm_scale * log2(e); K_hat = (e2m1 * s_blk) * g_K
-      qk_scale = a.sm_scale * 1.44269504088896341f * a.k_gscale * __builtin_ldexpf(1.0f, -qexp);
-    };
-    float thr = -INFINITY;    // raw score above which the running maximum must be raised
-
-    // Every load below is unconditional: a pair index past the end is clamped to the last pair (a
-    // re-read that hits in cache) and an odd trailing page is masked, so no branch separates a load
-    // from its use and the waits on the vector-memory counter stay precise while two pairs are in flight.
-    const int npairs = (pg_end - pg_begin + 1) >> 1;
-    // the wave's slice of the page table as a buffer; ids are read with a scalar offset
-    const __amdgpu_buffer_rsrc_t ids_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int32_t*>(pt + pg_begin), 0, (pg_end - pg_begin) * 4, kBufferWord3);
-    int vzero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));   // per-lane zero offset: keeps these on the vector path
-    auto load_ids = [&](int pair, int& i0, int& i1) {
-      const int rel = 2 * min(pair, npairs - 1);
-      i0 = (int)__builtin_amdgcn_raw_buffer_load_b32(ids_rsrc, vzero, rel * 4, 0);
-      i1 = (int)__builtin_amdgcn_raw_buffer_load_b32(ids_rsrc, vzero, min(rel + 1, pg_end - pg_begin - 1) * 4, 0);
-    };
-    auto issue = [&](Page& p0, Page& p1, int i0, int i1) {
-      load_page(p0, a, (size_t)__builtin_amdgcn_readfirstlane(i0) * a.hkv + hk, (unsigned)lane);
-      load_page(p1, a, (size_t)__builtin_amdgcn_readfirstlane(i1) * a.hkv + hk, (unsigned)lane);
-    };
-
-    // S^T = K_hat q^T for one pair of pages (two independent MFMA chains).  Only the last pair of a
-    // wave's range can hold a partly filled or missing page (tail): masking runs only there.
-    auto scores = [&](Page& p0, Page& p1, int pair, bool tail, float (&x)[8]) {
-      const int pg = pg_begin + 2 * pair;
-      int nv0 = kPageSize, nv1 = kPageSize;
-      if (tail) {
-        asm volatile("" ::: "memory");   // keep this a branch: the masking must not run on every pair
-        nv0 = min(kPageSize, seq_len - pg * kPageSize);
-        nv1 = (pg + 1 < pg_end) ? min(kPageSize, seq_len - (pg + 1) * kPageSize) : 0;
-        const int ln = opaque_lane_id();
-        if (nv0 < kPageSize) mask_page(p0, nv0, ln);
-        if (nv1 < kPageSize) mask_page(p1, nv1, ln);   // nv1 == 0: a duplicated page, all masked
-      }
-      const h2 sc0 = k_scales(p0), sc1 = k_scales(p1);
-      f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<0>(p0, sc0), qb[0], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<0>(p1, sc1), qb[0], s1, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<1>(p0, sc0), qb[1], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<1>(p1, sc1), qb[1], s1, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<2>(p0, sc0), qb[2], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<2>(p1, sc1), qb[2], s1, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p0, sc0), qb[3], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p1, sc1), qb[3], s1, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[r] = s0[r];
-        x[4 + r] = s1[r];
-      }
-      if (tail) {
-        asm volatile("" ::: "memory");
-        const int t0 = 4 * (opaque_lane_id() >> 4);   // first token row of this lane
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (t0 + r >= nv0) x[r] = -INFINITY;
-          if (t0 + r >= nv1) x[4 + r] = -INFINITY;
+      if constexpr (std::is_same<Page, PageNv4>::value) {
+        if (a.new_k != nullptr) {
+          const int pos = seq_len - 1;
+          if (pos / kPageSize >= pg_begin && pos / kPageSize < pg_end) {
+            append_token_nvfp4(a, b, hk, pos, pt[pos / kPageSize], lane);
+            // only this wave reads the page back; its stores reach L2 (L1 writes through, and L1 holds no
+            // copy of the page: it is invalidated at kernel start), so waiting for them suffices
+            __threadfence_block();
+          }
         }
       }
-    };
 
-    // Online softmax over one pair's raw scores, then O^T += V_hat^T P^T.
-    auto accumulate = [&](const Page& p0, const Page& p1, const float (&x)[8]) {
-      v_scale_publish(p0, vs_slot, lane);
-      v_scale_publish(p1, vs_slot + 64, lane);
-      const uint32_t* vq0 = vs_slot + 16 * c;
-      const uint32_t* vq1 = vs_slot + 64 + 16 * c;
-      const float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      if (__any(xm > thr)) {   // some weight would exceed 2^kSlack: raise every head's running maximum
-        const float hmax = max_xor32(max_xor16(xm));
-        const float m_new = fmaxf(m_run, hmax * qk_scale);   // qk_scale > 0: the max commutes with it
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) o[n] *= alpha;
-        m_run = m_new;
-        thr = (m_run + kSlack) / qk_scale;
-      }
-      float pr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk_scale, -m_run));
-      l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-      // P = hi + lo in fp16: hi rounds toward zero, lo = fp16(P - hi) keeps ~11 more bits
-      h2 ph2[4], pl2[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        ph2[k] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2 * k], pr[2 * k + 1]));
-        pl2[k] = lo_part(pr[2 * k], pr[2 * k + 1], ph2[k]);
-      }
-      if constexpr (kPack) {
-        h2 pp[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) pp[k] = lo_lane ? pl2[k] : ph2[k];
-        const h8 pb = cat4(pp[0], pp[1], pp[2], pp[3]);
-        static_for<0, 8>([&](auto nc) {
-          constexpr int N = decltype(nc)::value;
-          o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<N>(p0, p1, vq0, vq1), pb, o[N], 0, 0, 0);
-        });
-      } else {
-        const h8 ph = cat4(ph2[0], ph2[1], ph2[2], ph2[3]);
-        const h8 pl = cat4(pl2[0], pl2[1], pl2[2], pl2[3]);
-        // hi product of block N issued next to the lo product of block N-1
-        h8 va_prev;
-        static_for<0, 8>([&](auto nc) {
-          constexpr int N = decltype(nc)::value;
-          const h8 va = v_operand<N>(p0, p1, vq0, vq1);
-          o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, o[N], 0, 0, 0);
-          if constexpr (N > 0) o[N - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[N - 1], 0, 0, 0);
-          va_prev = va;
-        });
-        o[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[7], 0, 0, 0);
-      }
-    };
+      float m_run = -INFINITY, l_run = 0.0f;
+      f4 o[8];
+    #pragma unroll
+      for (int n = 0; n < 8; ++n) o[n] = f4{0.f, 0.f, 0.f, 0.f};
 
-    // Software pipeline: the scores of pair p+1 are computed right after pair p's PV products are
-    // issued, so the matrix cores and the next pair's decode overlap the softmax dependency chain.
-    float x[8];
-    if constexpr (std::is_same<Page, PageNv4>::value) {
-      // Three register buffers in rotation: two pairs are in flight while one is computed; page ids
-      // are fetched one pair ahead of the data that needs them.
-      Page pa0, pa1, pb0, pb1, pc0, pc1;
-      int a0, a1, b0, b1, c0, c1;
-      load_ids(0, a0, a1);
-      load_ids(1, b0, b1);
-      load_ids(2, c0, c1);
-      load_q();
-      issue(pa0, pa1, a0, a1);
-      issue(pb0, pb1, b0, b1);
-      prep_q();
-      scores(pa0, pa1, 0, npairs <= 1, x);
-      for (int pr = 0;; pr += 3) {
-        issue_priority(npairs - pr, npairs);
-        load_ids(pr + 3, a0, a1);
-        issue(pc0, pc1, c0, c1);
-        accumulate(pa0, pa1, x);
-        if (pr + 1 >= npairs) break;
-        scores(pb0, pb1, pr + 1, pr + 2 >= npairs, x);
-        load_ids(pr + 4, b0, b1);
-        issue(pa0, pa1, a0, a1);
-        accumulate(pb0, pb1, x);
-        if (pr + 2 >= npairs) break;
-        scores(pc0, pc1, pr + 2, pr + 3 >= npairs, x);
-        load_ids(pr + 5, c0, c1);
-        issue(pb0, pb1, b0, b1);
-        accumulate(pc0, pc1, x);
-        if (pr + 3 >= npairs) break;
-        scores(pa0, pa1, pr + 3, pr + 4 >= npairs, x);
-      }
-    } else {
-      // FP8 pages take twice the registers: two buffers, one pair in flight while one is computed.
-      Page pa0, pa1, pb0, pb1;
-      int a0, a1, b0, b1;
-      load_ids(0, a0, a1);
-      load_ids(1, b0, b1);
-      load_q();
-      issue(pa0, pa1, a0, a1);
-      prep_q();
-      scores(pa0, pa1, 0, npairs <= 1, x);
-      for (int pr = 0;; pr += 2) {
-        issue_priority(npairs - pr, npairs);
-        load_ids(pr + 2, a0, a1);
-        issue(pb0, pb1, b0, b1);
-        accumulate(pa0, pa1, x);
-        if (pr + 1 >= npairs) break;
-        scores(pb0, pb1, pr + 1, pr + 2 >= npairs, x);
-        load_ids(pr + 3, b0, b1);
-        issue(pa0, pa1, a0, a1);
-        accumulate(pb0, pb1, x);
-        if (pr + 2 >= npairs) break;
-        scores(pa0, pa1, pr + 2, pr + 3 >= npairs, x);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    l_run = sum_xor32(sum_xor16(l_run));
-    if constexpr (kPack) {
-#pragma unroll
-      for (int n = 0; n < 8; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[n][r] += from_lane_xor8(o[n][r]);
-    }
-  }
+      if (pg_begin < pg_end) {
+        // q row -> fp16 B operands, rescaled by a power of two so the row maximum sits in [2^13, 2^14).
+        // The raw row is loaded with the first page ids (every lane reads a valid row: absent heads
+        // read head 0 and zero it), and converted while the first pages are in flight, so the wave
+        // waits for two memory round trips before its first scores, not three.
+        h8 qb[4];
+        float qk_scale = 0.0f;
+        uint4 q_raw[4];
+        auto load_q = [&] {
+          const uint4* qp =
+              reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + row * kHeadDim + 32 * c);
+    #pragma unroll
+          for (int i = 0; i < 4; ++i) q_raw[i] = qp[i];
+        };
+        auto prep_q = [&] {
+          float qf[32];
+    #pragma unroll
+          for (int i = 0; i < 4; ++i) bf16x8_to_f32(q_raw[i], qf + 8 * i);
+    #pragma unroll
+          for (int i = 0; i < 32; ++i) qf[i] = head_ok ? qf[i] : 0.0f;
+          float qmax = 0.0f;
+    #pragma unroll
+          for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qf[i]));
+          qmax = max_xor16(qmax);
+          qmax = max_xor32(qmax);
+          int qexp = 0;
+          if (qmax > 0.0f) {
+            int ex;
+            (void)frexpf(qmax, &ex);          // qmax = f * 2^ex, f in [0.5, 1)
+            qexp = min(max(14 - ex, -100), 100);
+          }
+    #pragma unroll
+          for (int s = 0; s < 4; ++s)
+    #pragma unroll
+            for (int i = 0; i < 8; ++i) qb[s][i] = (_Float16)__builtin_ldexpf(qf[8 * s + i], qexp);
+          // scores in log2 units: <q, K_hat> * sm_scale * log2(e); K_hat = (e2m1 * s_blk) * g_K
+          qk_scale = a.sm_scale * 1.44269504088896341f * a.k_gscale * __builtin_ldexpf(1.0f, -qexp);
+        };
+        float thr = -INFINITY;    // raw score above which the running maximum must be raised
 
-  // ---- combine the 4 waves of this workgroup (lane holds O^T[16n + 4c + r][head jh]) ----
-  if (!lo_lane) {
-#pragma unroll
-    for (int n = 0; n < 8; ++n) *reinterpret_cast<f4*>(&red_o[wave][jh][16 * n + 4 * c]) = o[n];
-    if (c == 0) {
-      red_ml[wave][jh][0] = m_run;
-      red_ml[wave][jh][1] = l_run;
-    }
-  }
-  __syncthreads();
-  const int tj = threadIdx.x >> 4;            // query head (within the group) of this thread
-  const int td = (threadIdx.x & 15) * 8;      // first of its 8 channels
-  const bool t_ok = tj < group;
-  const size_t trow = (size_t)b * a.hq + hk * group + (t_ok ? tj : 0);
-  float cm = -INFINITY, cl = 0.0f, co[8];
-  if (t_ok) {
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (red_ml[w][tj][1] > 0.0f) cm = fmaxf(cm, red_ml[w][tj][0]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) co[i] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float lw = red_ml[w][tj][1];
-      if (lw > 0.0f) {
-        const float wt = __builtin_amdgcn_exp2f(red_ml[w][tj][0] - cm);
-        cl += wt * lw;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) co[i] += wt * red_o[w][tj][td + i];
-      }
-    }
-  }
-  if (a.num_splits == 1) {
-    if (t_ok) {
-      const float f = a.v_gscale / cl;
-      float* dst = a.out + trow * kHeadDim + td;
-      *reinterpret_cast<f4*>(dst) = f4{co[0], co[1], co[2], co[3]} * f;
-      *reinterpret_cast<f4*>(dst + 4) = f4{co[4], co[5], co[6], co[7]} * f;
-    }
-    return;
-  }
+        // Every load below is unconditional: a pair index past the end is clamped to the last pair (a
+        // re-read that hits in cache) and an odd trailing page is masked, so no branch separates a load
+        // from its use and the waits on the vector-memory counter stay precise while two pairs are in flight.
+        const int npairs = (pg_end - pg_begin + 1) >> 1;
+        // the wave's slice of the page table as a buffer; ids are read with a scalar offset
+        const __amdgpu_buffer_rsrc_t ids_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t*>(pt + pg_begin), 0, (pg_end - pg_begin) * 4, kBufferWord3);
+        int vzero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));   // per-lane zero offset: keeps these on the vector path
+        auto load_ids = [&](int pair, int& i0, int& i1) {
+          const int rel = 2 * min(pair, npairs - 1);
+          i0 = (int)__builtin_amdgcn_raw_buffer_load_b32(ids_rsrc, vzero, rel * 4, 0);
+          i1 = (int)__builtin_amdgcn_raw_buffer_load_b32(ids_rsrc, vzero, min(rel + 1, pg_end - pg_begin - 1) * 4, 0);
+        };
+        auto issue = [&](Page& p0, Page& p1, int i0, int i1) {
+          load_page(p0, a, (size_t)__builtin_amdgcn_readfirstlane(i0) * a.hkv + hk, (unsigned)lane);
+          load_page(p1, a, (size_t)__builtin_amdgcn_readfirstlane(i1) * a.hkv + hk, (unsigned)lane);
+        };
 
-  // ---- several splits: publish this workgroup's partial for the merge kernel ----
-  float* part_o = reinterpret_cast<float*>(a.workspace);
-  float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
-  if (t_ok) {
-    float* dst = part_o + (trow * a.num_splits + split) * kHeadDim + td;
-    *reinterpret_cast<f4*>(dst) = f4{co[0], co[1], co[2], co[3]} * a.v_gscale;
-    *reinterpret_cast<f4*>(dst + 4) = f4{co[4], co[5], co[6], co[7]} * a.v_gscale;
-    if (td == 0) *reinterpret_cast<float2*>(part_ml + (trow * a.num_splits + split) * 2) = make_float2(cm, cl);
+        // S^T = K_hat q^T for one pair of pages (two independent MFMA chains).  Only the last pair of a
+        // wave's range can hold a partly filled or missing page (tail): masking runs only there.
+        auto scores = [&](Page& p0, Page& p1, int pair, bool tail, float (&x)[8]) {
+          const int pg = pg_begin + 2 * pair;
+          int nv0 = kPageSize, nv1 = kPageSize;
+          if (tail) {
+            asm volatile("" ::: "memory");   // keep this a branch: the masking must not run on every pair
+            nv0 = min(kPageSize, seq_len - pg * kPageSize);
+            nv1 = (pg + 1 < pg_end) ? min(kPageSize, seq_len - (pg + 1) * kPageSize) : 0;
+            const int ln = opaque_lane_id();
+            if (nv0 < kPageSize) mask_page(p0, nv0, ln);
+            if (nv1 < kPageSize) mask_page(p1, nv1, ln);   // nv1 == 0: a duplicated page, all masked
+          }
+          const h2 sc0 = k_scales(p0), sc1 = k_scales(p1);
+          f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<0>(p0, sc0), qb[0], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<0>(p1, sc1), qb[0], s1, 0, 0, 0);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<1>(p0, sc0), qb[1], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<1>(p1, sc1), qb[1], s1, 0, 0, 0);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<2>(p0, sc0), qb[2], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<2>(p1, sc1), qb[2], s1, 0, 0, 0);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p0, sc0), qb[3], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p1, sc1), qb[3], s1, 0, 0, 0);
+    #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[r] = s0[r];
+            x[4 + r] = s1[r];
+          }
+          if (tail) {
+            asm volatile("" ::: "memory");
+            const int t0 = 4 * (opaque_lane_id() >> 4);   // first token row of this lane
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (t0 + r >= nv0) x[r] = -INFINITY;
+              if (t0 + r >= nv1) x[4 + r] = -INFINITY;
+            }
+          }
+        };
+
+        // Online softmax over one pair's raw scores, then O^T += V_hat^T P^T.
+        auto accumulate = [&](const Page& p0, const Page& p1, const float (&x)[8]) {
+          v_scale_publish(p0, vs_slot, lane);
+          v_scale_publish(p1, vs_slot + 64, lane);
+          const uint32_t* vq0 = vs_slot + 16 * c;
+          const uint32_t* vq1 = vs_slot + 64 + 16 * c;
+          const float xm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+          if (__any(xm > thr)) {   // some weight would exceed 2^kSlack: raise every head's running maximum
+            const float hmax = max_xor32(max_xor16(xm));
+            const float m_new = fmaxf(m_run, hmax * qk_scale);   // qk_scale > 0: the max commutes with it
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+    #pragma unroll
+            for (int n = 0; n < 8; ++n) o[n] *= alpha;
+            m_run = m_new;
+            thr = (m_run + kSlack) / qk_scale;
+          }
+          float pr[8];
+    #pragma unroll
+          for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk_scale, -m_run));
+          l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+          // P = hi + lo in fp16: hi rounds toward zero, lo = fp16(P - hi) keeps ~11 more bits
+          h2 ph2[4], pl2[4];
+    #pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            ph2[k] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2 * k], pr[2 * k + 1]));
+            pl2[k] = lo_part(pr[2 * k], pr[2 * k + 1], ph2[k]);
+          }
+          if constexpr (kPack) {
+            h2 pp[4];
+    #pragma unroll
+            for (int k = 0; k < 4; ++k) pp[k] = lo_lane ? pl2[k] : ph2[k];
+            const h8 pb = cat4(pp[0], pp[1], pp[2], pp[3]);
+            static_for<0, 8>([&](auto nc) {
+              constexpr int N = decltype(nc)::value;
+              o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<N>(p0, p1, vq0, vq1), pb, o[N], 0, 0, 0);
+            });
+          } else {
+            const h8 ph = cat4(ph2[0], ph2[1], ph2[2], ph2[3]);
+            const h8 pl = cat4(pl2[0], pl2[1], pl2[2], pl2[3]);
+            // hi product of block N issued next to the lo product of block N-1
+            h8 va_prev;
+            static_for<0, 8>([&](auto nc) {
+              constexpr int N = decltype(nc)::value;
+              const h8 va = v_operand<N>(p0, p1, vq0, vq1);
+              o[N] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, o[N], 0, 0, 0);
+              if constexpr (N > 0) o[N - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[N - 1], 0, 0, 0);
+              va_prev = va;
+            });
+            o[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va_prev, pl, o[7], 0, 0, 0);
+          }
+        };
+
+        // Software pipeline: the scores of pair p+1 are computed right after pair p's PV products are
+        // issued, so the matrix cores and the next pair's decode overlap the softmax dependency chain.
+        float x[8];
+        if constexpr (std::is_same<Page, PageNv4>::value) {
+          // Three register buffers in rotation: two pairs are in flight while one is computed; page ids
+          // are fetched one pair ahead of the data that needs them.
+          Page pa0, pa1, pb0, pb1, pc0, pc1;
+          int a0, a1, b0, b1, c0, c1;
+          load_ids(0, a0, a1);
+          load_ids(1, b0, b1);
+          load_ids(2, c0, c1);
+          load_q();
+          issue(pa0, pa1, a0, a1);
+          issue(pb0, pb1, b0, b1);
+          prep_q();
+          scores(pa0, pa1, 0, npairs <= 1, x);
+          for (int pr = 0;; pr += 3) {
+            issue_priority(npairs - pr, npairs);
+            load_ids(pr + 3, a0, a1);
+            issue(pc0, pc1, c0, c1);
+            accumulate(pa0, pa1, x);
+            if (pr + 1 >= npairs) break;
+            scores(pb0, pb1, pr + 1, pr + 2 >= npairs, x);
+            load_ids(pr + 4, b0, b1);
+            issue(pa0, pa1, a0, a1);
+            accumulate(pb0, pb1, x);
+            if (pr + 2 >= npairs) break;
+            scores(pc0, pc1, pr + 2, pr + 3 >= npairs, x);
+            load_ids(pr + 5, c0, c1);
+            issue(pb0, pb1, b0, b1);
+            accumulate(pc0, pc1, x);
+            if (pr + 3 >= npairs) break;
+            scores(pa0, pa1, pr + 3, pr + 4 >= npairs, x);
+          }
+        } else {
+          // FP8 pages take twice the registers: two buffers, one pair in flight while one is computed.
+          Page pa0, pa1, pb0, pb1;
+          int a0, a1, b0, b1;
+          load_ids(0, a0, a1);
+          load_ids(1, b0, b1);
+          load_q();
+          issue(pa0, pa1, a0, a1);
+          prep_q();
+          scores(pa0, pa1, 0, npairs <= 1, x);
+          for (int pr = 0;; pr += 2) {
+            issue_priority(npairs - pr, npairs);
+            load_ids(pr + 2, a0, a1);
+            issue(pb0, pb1, b0, b1);
+            accumulate(pa0, pa1, x);
+            if (pr + 1 >= npairs) break;
+            scores(pb0, pb1, pr + 1, pr + 2 >= npairs, x);
+            load_ids(pr + 3, b0, b1);
+            issue(pa0, pa1, a0, a1);
+            accumulate(pb0, pb1, x);
+            if (pr + 2 >= npairs) break;
+            scores(pa0, pa1, pr + 2, pr + 3 >= npairs, x);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        l_run = sum_xor32(sum_xor16(l_run));
+        if constexpr (kPack) {
+    #pragma unroll
+          for (int n = 0; n < 8; ++n)
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) o[n][r] += from_lane_xor8(o[n][r]);
+        }
+      }
+
+      // ---- combine the 4 waves of this workgroup (lane holds O^T[16n + 4c + r][head jh]) ----
+      if (!lo_lane) {
+    #pragma unroll
+        for (int n = 0; n < 8; ++n) *reinterpret_cast<f4*>(&red_o[wave][jh][16 * n + 4 * c]) = o[n];
+        if (c == 0) {
+          red_ml[wave][jh][0] = m_run;
+          red_ml[wave][jh][1] = l_run;
+        }
+      }
+      __syncthreads();
+      const int tid = (wave << 6) | opaque_lane_id();
+      const int tj = tid >> 4;                    // query head (within the group) of this thread
+      const int td = (tid & 15) * 8;              // first of its 8 channels
+      if (tj < group) {
+        float cm = -INFINITY, cl = 0.0f, co[8];
+    #pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          if (red_ml[w][tj][1] > 0.0f) cm = fmaxf(cm, red_ml[w][tj][0]);
+    #pragma unroll
+        for (int i = 0; i < 8; ++i) co[i] = 0.0f;
+    #pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float lw = red_ml[w][tj][1];
+          if (lw > 0.0f) {
+            const float wt = __builtin_amdgcn_exp2f(red_ml[w][tj][0] - cm);
+            cl += wt * lw;
+    #pragma unroll
+            for (int i = 0; i < 8; ++i) co[i] += wt * red_o[w][tj][td + i];
+          }
+        }
+        if (whole) {
+          const float f = a.v_gscale / cl;
+          float* dst = a.out + ((size_t)b * a.hq + hk * group + tj) * kHeadDim + td;
+          *reinterpret_cast<f4*>(dst) = f4{co[0], co[1], co[2], co[3]} * f;
+          *reinterpret_cast<f4*>(dst + 4) = f4{co[4], co[5], co[6], co[7]} * f;
+        } else {
+          const size_t slots = (size_t)a.num_splits + (size_t)a.batch * a.hkv;
+          const size_t e = ((size_t)blockIdx.x + (size_t)b * a.hkv + hk) * group + tj;
+          float* part_o = reinterpret_cast<float*>(a.workspace);
+          float* part_ml = part_o + slots * group * kHeadDim;
+          float* dst = part_o + e * kHeadDim + td;
+          *reinterpret_cast<f4*>(dst) = f4{co[0], co[1], co[2], co[3]} * a.v_gscale;
+          *reinterpret_cast<f4*>(dst + 4) = f4{co[4], co[5], co[6], co[7]} * a.v_gscale;
+          if (td == 0) *reinterpret_cast<float2*>(part_ml + e * 2) = make_float2(cm, cl);
+        }
+      }
+
+    }
+
+    // ---- next stream of the piece ----
+    u0 = s_start + n_pages + extra;
+    if (u0 >= u1) return;
+    s_start = u0;
+    if (++hk == a.hkv) {
+      hk = 0;
+      ++b;
+      seq_len = next_len;
+      n_pages = seq_pages(seq_len);
+    }
+    if (has_pages) __syncthreads();   // the combine above has read red_o / red_ml before they are written again
   }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, query head) per block, over the splits that
-// sequence has (a short sequence of a ragged batch writes fewer than num_splits): 8 groups of 32
-// threads, group g taking splits g, g + 8, g + 16, ... with a running maximum (4 channels per
-// thread), then the 8 group states are combined through LDS.  The first two splits of every group
-// are read together with the sequence length, at indices clamped into the row's num_splits entries,
-// before the split count is known (an entry past the count was not written by this launch and is
-// dropped unused): up to 16 splits the merge waits for one memory round trip.
+// Log-sum-exp merge of the partials of one (sequence, query head) per block.  The block finds the
+// pieces its stream spans from the sequence lengths (as the split kernel does); a stream inside one
+// piece was written out by the split kernel and the block exits.  Otherwise 8 groups of 32 threads
+// take partials g, g + 8, g + 16, ... with a running maximum (4 channels per thread), and the 8
+// group states are combined through LDS.
 constexpr int kMergeGroups = 8;
 __device__ __forceinline__ void merge_one(float2 vc, const f4& oc, float& m, float& den, f4& acc) {
   if (vc.y > 0.0f) {   // empty splits carry no partial output
@@ -621,30 +702,51 @@ __device__ __forceinline__ void merge_one(float2 vc, const f4& oc, float& m, flo
   }
 }
 __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml, int num_splits,
-                                                           const int32_t* __restrict__ seq_lens, int hq,
-                                                           int pages_per_split, float* __restrict__ out) {
-  const size_t row = blockIdx.x;
+                                                           const float* __restrict__ part_ml,
+                                                           const int32_t* __restrict__ seq_lens, int batch, int hq,
+                                                           int hkv, int pieces, int min_pages,
+                                                           float* __restrict__ out) {
+  const int row = (int)blockIdx.x;
+  const int b = row / hq, h = row - b * hq;
+  const int group = hq / hkv, hk = h / group, j = h - hk * group;
+  const int lane = threadIdx.x & 63;
+  // pages of the whole step and of the sequences before b, and the length range (each wave
+  // computes the same values); units as in the split kernel
+  int total = 0, before = 0, lmin = 0x7FFFFFFF, lmax = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int bl = base + lane;
+    const int len = bl < batch ? seq_lens[bl] : 0;
+    const int pg = bl < batch ? seq_pages(len) : 0;
+    total += wave_sum(pg);
+    before += wave_sum(bl < b ? pg : 0);
+    lmin = min(lmin, wave_min(bl < batch ? len : 0x7FFFFFFF));
+    lmax = max(lmax, wave_max(len));
+  }
+  const int extra = lmin == lmax ? 0 : kStreamCostPages;
+  const int n_pages = seq_pages(seq_lens[b]);
+  const int pp = piece_pages((total + extra * batch) * hkv, pieces, min_pages);
+  const int r0 = ((before + extra * b) * hkv + hk * (n_pages + extra)) + extra;   // first page's unit
+  const int first = r0 / pp;
+  const int n = (r0 + n_pages - 1) / pp - first + 1;   // pieces holding pages of the stream
+  if (n == 1) return;
   const int g = threadIdx.x >> 5;
   const int d = (threadIdx.x & 31) * 4;
-  const float2* ml = reinterpret_cast<const float2*>(part_ml) + row * num_splits;
-  const float* po = part_o + row * num_splits * kHeadDim + d;
-  const int seq_len = seq_lens[row / (unsigned)hq];
-  const int s0 = min(g, num_splits - 1), s1 = min(g + kMergeGroups, num_splits - 1);
-  const float2 v0 = ml[s0], v1 = ml[s1];
-  const f4 o0 = *reinterpret_cast<const f4*>(po + (size_t)s0 * kHeadDim);
-  const f4 o1 = *reinterpret_cast<const f4*>(po + (size_t)s1 * kHeadDim);
-  // all five reads in flight together (the compiler would otherwise sink the partials' reads
-  // below the split count they do not depend on)
-  asm volatile("" ::"s"(seq_len), "v"(v0.x), "v"(v0.y), "v"(v1.x), "v"(v1.y), "v"(o0[0]), "v"(o0[1]), "v"(o0[2]),
-               "v"(o0[3]), "v"(o1[0]), "v"(o1[1]), "v"(o1[2]), "v"(o1[3]));
-  const int n_split_b = seq_splits((seq_len + kPageSize - 1) / kPageSize, pages_per_split, num_splits);
+  const size_t e0 = ((size_t)first + (size_t)b * hkv + hk) * group + j;   // entry of its first partial
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + e0;
+  const float* po = part_o + e0 * kHeadDim + d;
+  const size_t stride = group;   // entries between consecutive partials of the stream
+  // the first two partials of every group are read together, at indices clamped into the stream's
+  // (an entry past its count is a re-read and dropped): up to 16 partials, one memory round trip
+  const int i0 = min(g, n - 1), i1 = min(g + kMergeGroups, n - 1);
+  const float2 v0 = ml[i0 * stride], v1 = ml[i1 * stride];
+  const f4 o0 = *reinterpret_cast<const f4*>(po + i0 * stride * kHeadDim);
+  const f4 o1 = *reinterpret_cast<const f4*>(po + i1 * stride * kHeadDim);
   float m = -INFINITY, den = 0.0f;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (g < n_split_b) merge_one(v0, o0, m, den, acc);
-  if (g + kMergeGroups < n_split_b) merge_one(v1, o1, m, den, acc);
-  for (int s = g + 2 * kMergeGroups; s < n_split_b; s += kMergeGroups)   // more than 16 splits
-    merge_one(ml[s], *reinterpret_cast<const f4*>(po + (size_t)s * kHeadDim), m, den, acc);
+  if (g < n) merge_one(v0, o0, m, den, acc);
+  if (g + kMergeGroups < n) merge_one(v1, o1, m, den, acc);
+  for (int i = g + 2 * kMergeGroups; i < n; i += kMergeGroups)   // more than 16 partials
+    merge_one(ml[i * stride], *reinterpret_cast<const f4*>(po + i * stride * kHeadDim), m, den, acc);
   __shared__ float g_m[kMergeGroups], g_den[kMergeGroups];
   __shared__ f4 g_acc[kMergeGroups][32];
   if ((threadIdx.x & 31) == 0) {
@@ -668,7 +770,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restri
       aa += w * g_acc[i][threadIdx.x];
     }
   }
-  *reinterpret_cast<f4*>(out + row * kHeadDim + d) = aa * (1.0f / dd);
+  *reinterpret_cast<f4*>(out + (size_t)row * kHeadDim + d) = aa * (1.0f / dd);
 }
 
 // Library-held split partials for callers that cannot allocate: one array per device, reached by
@@ -700,7 +802,7 @@ hipError_t decode_scratch(void** ptr) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  const dim3 grid((unsigned)a.num_splits * a.batch * a.hkv);
+  const dim3 grid((unsigned)a.num_splits);
   // the extended launch lets the dispatch packet itself record the events: no extra stream commands
   const bool pack = a.hq / a.hkv <= 8;
   const dim3 block(64 * kWaves);
@@ -717,10 +819,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t sta
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
+  const size_t slots = (size_t)a.num_splits + (size_t)a.batch * a.hkv;
   const float* part_o = reinterpret_cast<const float*>(a.workspace);
-  const float* part_ml = part_o + (size_t)a.batch * a.hq * a.num_splits * kHeadDim;
-  hipLaunchKernelGGL(merge_splits_kernel, dim3(a.batch * a.hq), dim3(256), 0, stream, part_o, part_ml, a.num_splits,
-                     a.seq_lens, a.hq, a.pages_per_split, a.out);
+  const float* part_ml = part_o + slots * (a.hq / a.hkv) * kHeadDim;
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(a.batch * a.hq), dim3(256), 0, stream, part_o, part_ml, a.seq_lens,
+                     a.batch, a.hq, a.hkv, a.num_splits, a.pages_per_split, a.out);
   return hipGetLastError();
 }
 

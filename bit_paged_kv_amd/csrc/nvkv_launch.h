@@ -35,8 +35,8 @@ hipError_t launch_extend_attn(const void* q, const int32_t* chunk_offsets, const
                               float v_ws_scale, float sm_scale, int batch, int hq, int hkv, int max_chunk,
                               float* out, hipStream_t stream);
 
-// Decode: one workgroup of four wavefronts per (sequence, kv head, split); with several splits a
-// second kernel merges the partial softmax states.
+// Decode: the step's pages are cut into num_splits equal pieces, one workgroup of four wavefronts
+// each; streams split over several pieces leave partial softmax states that a second kernel merges.
 enum CacheFormat { kFmtNvfp4 = 0, kFmtFp8 = 1 };
 
 struct DecodeArgs {
@@ -52,7 +52,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   int batch, hq, hkv;
   float sm_scale;
-  int pages_per_split, num_splits;
+  int pages_per_split, num_splits;   // minimum piece size (pages), pieces = workgroups
   const void* new_k;          // NVFP4 fused append, or null
   const void* new_v;
   float* out;                 // fp32 [B][Hq][128]
@@ -61,9 +61,14 @@ struct DecodeArgs {
 
 size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits);
 
+// Cost, in pages, that the decode partition charges for each stream of a batch whose lengths
+// differ: the start-up of a segment (two memory round trips and the combine) measured against the
+// time a workgroup takes per page.
+constexpr int kStreamCostPages = 32;
+
 // Split partials held by the library for the no-allocation decode entry point: a 32 MiB array per
-// device, room for 64,527 (query row, split) partials of 130 floats (e.g. 64 sequences x 64 query
-// heads x 15 splits); its device address is resolved once per device.
+// device, room for 64,527 partial rows of 130 floats (e.g. 7553 pieces + 512 streams of 8 query
+// heads); its device address is resolved once per device.
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 constexpr int kMaxScratchDevices = 64;
 // Device address of the current device's array (hipGetSymbolAddress, cached per device).

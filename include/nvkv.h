@@ -121,25 +121,33 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
                            uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream);
 
 /*
- * Split planning for decode.  A sequence of P pages is cut into n = min(num_splits,
- * ceil(P / pages_per_split)) splits (at least one) of pages_per_split pages, the last taking the
- * remainder; each (sequence, kv head, split < n) is one workgroup of four wavefronts (each takes a
- * contiguous quarter of the split and the four combine in LDS), the grid's workgroups for splits
- * >= n exit at once, and with several splits a second kernel merges the n partial softmax states.
- * nvkv_plan_decode picks num_splits from host-side hints so that the grid fills the GPU (exactly
- * two workgroups per compute unit when the lengths are equal and the stream count batch *
- * num_kv_heads allows it, else about three, or 4.5 for a ragged batch):
+ * Split planning for decode.  The step's work -- the pages of every (sequence b, kv head h) stream,
+ * in that order -- is cut into num_splits equal pieces, one workgroup of four wavefronts each.
+ * When the sequence lengths differ, each stream is also charged a fixed cost of 32 pages (the
+ * start-up of a segment), so a piece that holds many short streams gets fewer pages.  A piece
+ * takes max(pages_per_split, the even ceiling of the step's cost / num_splits) units.
+ * A workgroup walks the streams its piece holds: the four wavefronts split each stream's part
+ * and combine in LDS.  A stream that lies in one piece is written out directly.  A stream split
+ * over several pieces leaves one partial softmax state per piece, and a second kernel merges them.
+ * nvkv_plan_decode picks num_splits from host-side hints: two pieces per compute unit (all
+ * resident at once), or fewer for a small step so that pieces keep at least 16 pages.
  *   max_seq_len  : the longest sequence (tokens, including an appended token), > 0.
  *   total_tokens : sum of sequence lengths if known, else 0 (then batch * max_seq_len is assumed).
- *   force_pages_per_split : > 0 forces the split size (rounded up to even); 0 = automatic.
- * Outputs *pages_per_split (even, >= 2) and *num_splits (>= 1) with
- * num_splits * pages_per_split * 16 >= max_seq_len.  A sequence longer than that still runs
- * correctly: its last split takes all the remaining pages.
+ *   force_pages_per_split : > 0 asks for pieces of that many pages (rounded up to even, at most the
+ *                  step); num_splits then covers the hinted step.  0 = automatic.
+ * Outputs *pages_per_split (>= 2, the minimum piece size) and *num_splits (>= 1).  Any plan
+ * computes the same attention (up to the order of the fp32 sums).  A step larger than the hints
+ * only makes the pieces larger.
  */
 NVKV_API int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long long total_tokens,
                      int force_pages_per_split, int* pages_per_split, int* num_splits);
 
-/* Workspace bytes for decode with the given plan (0 when num_splits == 1); contents need no init. */
+/*
+ * Workspace bytes for decode with the given plan: partial states for (num_splits + batch *
+ * num_kv_heads) pieces-by-streams of (num_q_heads / num_kv_heads) rows of 130 floats.  The size
+ * is 0 when num_splits == 1, because one piece holds every stream whole.  The contents need no
+ * initialisation.
+ */
 NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                            int num_splits);
 
@@ -154,7 +162,10 @@ NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_k
  * matrix cores, P enters PV as an fp16 hi + lo pair, output is fp32.
  *   q          : [batch][num_q_heads][128] bf16, device.
  *   page_table : [batch][max_pages_per_seq] int32, device.
- *   seq_lens   : [batch] int32, device, each >= 1 (includes the appended token when new_k != NULL).
+ *   seq_lens   : [batch] int32, device, each >= 1 and <= max_pages_per_seq * 16 (includes the
+ *                appended token when new_k != NULL).  NVKV_E_UNSUPPORTED when
+ *                batch * (max_pages_per_seq + 32) * num_kv_heads + 2 * num_splits or
+ *                num_splits * pages_per_split exceeds 2^31 - 1 (32-bit unit offsets).
  *   num_q_heads / num_kv_heads must be an integer in 1..16.
  *   pages_per_split, num_splits : from nvkv_plan_decode.
  *   new_k, new_v : NULL, or [batch][num_kv_heads][128] bf16: fused quantize-append of one token

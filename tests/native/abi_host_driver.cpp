@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <vector>
@@ -143,10 +144,13 @@ static void check_plans() {
             const int st = nvkv_plan_decode(b, h, L, tot, force, &pps, &ns);
             CHECK(st == NVKV_OK || st == NVKV_E_UNSUPPORTED);
             if (st != NVKV_OK) continue;
-            const long long pages = ((long long)L + 15) / 16;
+            long long pages = (long long)b * (((long long)L + 15) / 16);
+            if (tot > 0) pages = std::min(pages, (tot + 15LL * b) / 16);
+            const long long units = std::max(1LL, pages * h);
             CHECK(pps >= 2 && pps % 2 == 0 && ns >= 1);
-            CHECK((long long)ns * pps >= pages);
-            CHECK((long long)(ns - 1) * pps < pages || ns == 1);
+            CHECK((long long)ns * pps <= 0x7FFFFFFFLL);
+            if (force == 0) CHECK(pps == 2 && ns == std::min(512LL, (units + 15) / 16));
+            else CHECK((long long)ns * pps >= units && (long long)(ns - 1) * pps < units);
           }
   int pps, ns;
   CHECK(nvkv_plan_decode(0, 8, 10, 0, 0, &pps, &ns) == NVKV_E_INVAL);
@@ -154,8 +158,8 @@ static void check_plans() {
   CHECK(nvkv_plan_decode(1, 8, 10, -1, 0, &pps, &ns) == NVKV_E_INVAL);
   CHECK(nvkv_plan_decode(1, 8, 10, 0, -1, &pps, &ns) == NVKV_E_INVAL);
   CHECK(nvkv_plan_decode(1, 8, 10, 0, 0, nullptr, &ns) == NVKV_E_INVAL);
-  // the long-context plan: two workgroups per compute unit
-  CHECK(nvkv_plan_decode(4, 8, 131072, 4LL * 131072, 0, &pps, &ns) == NVKV_OK && pps == 512 && ns == 16);
+  // the long-context plan: two pieces per compute unit
+  CHECK(nvkv_plan_decode(4, 8, 131072, 4LL * 131072, 0, &pps, &ns) == NVKV_OK && pps == 2 && ns == 512);
 }
 
 static void check_decode() {
@@ -178,7 +182,9 @@ static void check_decode() {
       {[](Dec& x) { x.nk = A; }, NVKV_E_INVAL},          {[](Dec& x) { x.ns = 4, x.ws = 0; }, NVKV_E_WORKSPACE},
       {[](Dec& x) { x.ns = 4, x.wsb = 100; }, NVKV_E_WORKSPACE},
       {[](Dec& x) { x.ns = 4, x.ws = MIS; }, NVKV_E_INVAL},
-      {[](Dec& x) { x.ns = INT_MAX, x.b = 2, x.hkv = 2, x.hq = 2; }, NVKV_E_INVAL},
+      {[](Dec& x) { x.ns = INT_MAX, x.b = 2, x.hkv = 2, x.hq = 2; }, NVKV_E_UNSUPPORTED},
+      {[](Dec& x) { x.maxp = 1 << 30; }, NVKV_E_UNSUPPORTED},   // page-heads past 32 bits
+      {[](Dec& x) { x.ns = 1 << 28, x.pps = 8; }, NVKV_E_UNSUPPORTED},
   };
   for (auto& c : cases) {
     Dec x;
@@ -205,17 +211,17 @@ static void check_decode() {
   n.ns = 4;
   g_launches = 0;
   CHECK(n.run_noalloc() == NVKV_OK && g_launches == 1 && g_last_decode.workspace == g_scratch_anchor);
-  n.b = 64, n.hq = 64, n.hkv = 8, n.ns = 16;       // 34,078,720 B of partials > 32 MiB
+  n.b = 64, n.hq = 64, n.hkv = 8, n.ns = 7554;     // (7554 + 512) x 8 x 520 B of partials > 32 MiB
   g_launches = 0;
   CHECK(n.run_noalloc() == NVKV_E_SCRATCH && g_launches == 0);
-  n.ns = 15;
+  n.ns = 7553;
   CHECK(n.run_noalloc() == NVKV_OK && g_launches == 1);
   n.q = 0;
   CHECK(n.run_noalloc() == NVKV_E_INVAL);
   CHECK(nvkv_decode_noalloc_max_bytes() == (size_t)32 << 20);
   // workspace sizes
   CHECK(nvkv_decode_workspace_size(4, 64, 8, 128, 1) == 0);
-  CHECK(nvkv_decode_workspace_size(4, 64, 8, 128, 16) == (size_t)4 * 64 * 16 * 130 * 4);
+  CHECK(nvkv_decode_workspace_size(4, 64, 8, 128, 16) == (size_t)(16 + 32) * 8 * 130 * 4);
   CHECK(nvkv_decode_workspace_size(4, 64, 8, 64, 16) == 0);
   CHECK(nvkv_decode_workspace_size(0, 64, 8, 128, 16) == 0);
 }

@@ -50,32 +50,42 @@ def test_status_strings(lib):
     assert lib.version() >= 100
 
 
+def _units(b, hkv, L, tot):
+    pages = b * math.ceil(L / 16)
+    if tot > 0:
+        pages = min(pages, (tot + b * 15) // 16)
+    return pages * hkv
+
+
 @pytest.mark.parametrize("b,hkv,L,tot", [(4, 8, 131072, 0), (32, 8, 4096, 0), (1, 1, 1, 0), (1, 1, 256, 0),
                                          (64, 8, 32768, 500000), (44, 8, 8192, 0), (3, 2, 17, 40)])
-def test_plan_covers_the_longest_sequence(lib, b, hkv, L, tot):
+def test_plan_pieces(lib, b, hkv, L, tot):
+    """The automatic plan: at most two workgroups per CU (256 CUs assumed without a GPU), pieces of
+    at least 16 pages, and a minimum piece size that leaves the balancing to the kernel."""
     pps, ns = lib.plan_decode(b, hkv, L, tot)
-    pages = math.ceil(L / 16)
-    assert pps >= 2 and pps % 2 == 0 and ns >= 1
-    assert ns * pps >= pages
-    assert (ns - 1) * pps < pages          # no split starts past the end of the longest sequence
+    assert pps == 2 and 1 <= ns <= 512
+    assert ns == min(512, math.ceil(_units(b, hkv, L, tot) / 16))
 
 
 def test_plan_shapes(lib):
     """The planner's shapes on a 256-CU device (the count it assumes without a GPU, and MI355X's):
-    exactly two workgroups per CU when the stream count divides 512 and the lengths are equal,
-    about three otherwise, 4.5 for a ragged batch."""
-    assert lib.plan_decode(4, 8, 131072, 4 * 131072) == (512, 16)      # 32 streams x 16 = 512
-    assert lib.plan_decode(32, 8, 4096, 32 * 4096) == (128, 2)         # 256 streams x 2 = 512
-    assert lib.plan_decode(44, 8, 8192, 44 * 8192) == (240, 3)         # 352 streams: ~3 per CU
-    rag = workloads.config(3)                                          # ragged: ~4.5 per CU
-    assert lib.plan_decode(rag.batch, rag.h_kv, int(rag.total_lens.max()), int(rag.total_lens.sum())) == (224, 10)
-    assert lib.plan_decode(1, 1, 256, 256) == (8, 2)                   # short: splits stay >= 8 pages
+    two equal pieces per CU whenever the step has at least 512 x 16 page-heads; on equal lengths
+    whose stream count divides 512 the pieces fall on stream boundaries (the kernel's piece is
+    the even ceiling of units / pieces)."""
+    for args, pieces_per_stream in (((4, 8, 131072, 4 * 131072), 16), ((32, 8, 4096, 32 * 4096), 2)):
+        assert lib.plan_decode(*args) == (2, 512)
+        assert _units(*args) // 512 * pieces_per_stream == math.ceil(args[2] / 16)
+    assert lib.plan_decode(44, 8, 8192, 44 * 8192) == (2, 512)
+    rag = workloads.config(3)
+    assert lib.plan_decode(rag.batch, rag.h_kv, int(rag.total_lens.max()), int(rag.total_lens.sum())) == (2, 512)
+    assert lib.plan_decode(1, 1, 256, 256) == (2, 1)                    # one piece: no merge, no workspace
+    assert lib.plan_decode(3, 2, 100, 300) == (2, 3)                    # 42 page-heads: pieces of >= 16
 
 
 def test_plan_forced_split(lib):
-    assert lib.plan_decode(2, 2, 1000, 0, 6) == (6, math.ceil(63 / 6))
-    assert lib.plan_decode(2, 2, 1000, 0, 5) == (6, math.ceil(63 / 6))      # rounded up to even
-    assert lib.plan_decode(2, 2, 100, 0, 1000) == (8, 1)                     # capped at the sequence
+    assert lib.plan_decode(2, 2, 1000, 0, 6) == (6, math.ceil(252 / 6))      # 2 x 63 pages x 2 heads
+    assert lib.plan_decode(2, 2, 1000, 0, 5) == (6, math.ceil(252 / 6))      # rounded up to even
+    assert lib.plan_decode(2, 2, 100, 0, 1000) == (28, 1)                    # capped at the step
 
 
 def test_plan_rejects_bad_hints(lib):
@@ -85,10 +95,10 @@ def test_plan_rejects_bad_hints(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.decode_workspace_size(4, 64, 8, 1) == 0                   # one split: no partials
+    assert lib.decode_workspace_size(4, 64, 8, 1) == 0                   # one piece: no partials
     n = lib.decode_workspace_size(4, 64, 8, 16)
-    assert n == 4 * 64 * 16 * 130 * 4                                    # [row][split][128 + 2] fp32
-    assert lib.decode_workspace_size(1, 4, 1, 3) == 1 * 4 * 3 * 130 * 4
+    assert n == (16 + 4 * 8) * 8 * 130 * 4                               # [pieces + streams][group][128 + 2] fp32
+    assert lib.decode_workspace_size(1, 4, 1, 3) == (3 + 1) * 4 * 130 * 4
     assert lib._lib.nvkv_decode_workspace_size(4, 64, 8, 64, 16) == 0      # head_dim other than 128
 
 
@@ -115,6 +125,7 @@ def _decode(lib, **kw):
     (dict(gk=float("nan")), INVAL), (dict(gv=0.0), INVAL), (dict(gk=-1.0), INVAL), (dict(gk=float("inf")), INVAL),
     (dict(sm=0.0), INVAL), (dict(sm=float("nan")), INVAL),
     (dict(b=0), INVAL), (dict(maxp=0), INVAL), (dict(pps=0), INVAL), (dict(ns=0), INVAL),
+    (dict(maxp=1 << 30), UNSUP), (dict(ns=1 << 28, pps=8), UNSUP),   # page-heads / piece offsets past 32 bits
     (dict(nk=A), INVAL),                                    # new_k without new_v
     (dict(ns=4, ws=None, wsb=0), WS), (dict(ns=4, wsb=100), WS),   # workspace missing / too small
     (dict(ns=4, ws=MIS, wsb=1 << 20), INVAL),                        # misaligned workspace
@@ -149,13 +160,13 @@ def _decode_noalloc(lib, **kw):
     (dict(q=None), INVAL), (dict(kd=None), INVAL), (dict(out=MIS), INVAL), (dict(d=64), UNSUP),
     (dict(hq=64, hkv=2), UNSUP), (dict(gk=float("inf")), INVAL), (dict(sm=0.0), INVAL), (dict(ns=0), INVAL),
     (dict(nk=A), INVAL),
-    # partials beyond the library-held array: 64 x 64 rows x 16 splits x 520 B = 34,078,720 B > 32 MiB
-    (dict(b=64, hq=64, hkv=8, ns=16), SCRATCH),
-    (dict(b=64, hq=64, hkv=8, ns=16, q=None), INVAL),       # argument errors are reported first
+    # partials beyond the library-held array: (7554 pieces + 512 streams) x 8 heads x 520 B > 32 MiB
+    (dict(b=64, hq=64, hkv=8, ns=7554), SCRATCH),
+    (dict(b=64, hq=64, hkv=8, ns=7554, q=None), INVAL),     # argument errors are reported first
 ])
 def test_noalloc_decode_validation(lib, kw, want):
     assert lib.decode_noalloc_max_bytes() == 32 << 20
-    assert lib.decode_workspace_size(64, 64, 8, 15) <= 32 << 20 < lib.decode_workspace_size(64, 64, 8, 16)
+    assert lib.decode_workspace_size(64, 64, 8, 7553) <= 32 << 20 < lib.decode_workspace_size(64, 64, 8, 7554)
     assert _decode_noalloc(lib, **kw) == want
 
 

@@ -71,8 +71,8 @@ def test_decode_split_count_invariance(nv, ragged):
 
 @pytest.mark.parametrize("plan", [(2, 3), (3, 2), (5, 1), (7, 4)])
 def test_decode_plan_shorter_than_sequences(nv, ragged, plan):
-    """Plans whose num_splits x pages_per_split pages do not cover the longest sequences: each
-    sequence's splits grow to hold all of its pages."""
+    """Plans whose num_splits x pages_per_split units do not cover the step (and odd minimum piece
+    sizes): the pieces grow to the even ceiling of the step's cost over num_splits."""
     wl, pool, gk, gv, want = ragged
     pt, sl = H.gpu_tables(wl, DEV)
     got = nv.nvfp4_decode(wl.q().to(DEV), pool, float(gk), float(gv), pt, sl, wl.sm_scale, plan, wl.h_kv)
