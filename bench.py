@@ -126,7 +126,7 @@ def host_cpu():
             "worker_cap": CPU_WORKER_CAP,
             "cap_reason": "one spawned worker per affinity core, at most 16: the host-CPU share of one GPU"}
 
-# HBM traffic of one decode step (decode_split_kernel + merge_splits_kernel) on the long workload, from
+# HBM traffic of one decode step (one decode_split_kernel launch, merge included) on the long workload, from
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch, one counter per run) scaled by
 # the factors a plain 1 GiB device copy gives (x2.000 / x1.000).  Valid only for the kernel sources
 # (the decode file and the headers it includes, hashed together) and the split plan they were taken
@@ -629,7 +629,7 @@ def main():
         kernel_bytes = step_bytes
         desc = (f"{name}: batch {wl.batch}, context {int(wl.seq_lens[0]) if name != 'ragged' else 'ragged'}, "
                 f"{wl.h_kv} KV / {wl.h_q} query heads, head_dim 128, page 16, NVFP4 cache, "
-                f"split-K {plan[1]} x {plan[0]} pages")
+                f"{plan[1]} equal pieces (at least {plan[0]} pages), split streams merged in-kernel")
         extra = {"batch": wl.batch, "context_tokens": int(wl.total_lens.sum()), "kv_heads": wl.h_kv,
                  "q_heads": wl.h_q, "head_dim": 128, "page_size": 16, "cache": "nvfp4",
                  "pages_per_split": plan[0], "num_splits": plan[1], "cache_copies_rotated": copies,
@@ -874,14 +874,14 @@ def main():
                   f"{min(kms) * 1e3:.1f} us, max {max(kms) * 1e3:.1f} us), timing-only HIP events (no system "
                   f"fence) recorded on the launch stream around each launch")
     elif timed_kernel:
-        # The decode step is two back-to-back kernels (split kernel, then the log-sum-exp merge when
-        # there are several splits).  The roofline unit is the step: its duration comes from the HIP
-        # events around the K timed steps (on the launch stream), which hold nothing else; a kernel
-        # trace of the same command shows the two kernels and the gap between them adding up to it.
+        # The decode step is one kernel launch (the last piece of each split stream merges it).  The
+        # roofline unit is the step: its duration comes from the HIP events around the K timed steps
+        # (on the launch stream), which hold nothing else; a kernel trace of the same command shows
+        # the launches back to back.
         kernel_ms = step_gpu_ms
         achieved = kernel_bytes / (kernel_ms * 1e-3) / 1e9
-        # the split kernel alone, for reference: KERNEL_SAMPLES more steps whose split-kernel dispatch
-        # records timing-only events (the recording itself adds a few microseconds inside the bracket)
+        # the kernel by itself, for reference: KERNEL_SAMPLES more steps whose kernel dispatch records
+        # timing-only events (the recording itself adds a few microseconds inside the bracket)
         events = HipEventPairs(KERNEL_SAMPLES)
         for i in range(KERNEL_SAMPLES):
             step(events, i)
@@ -892,10 +892,9 @@ def main():
         split_only = {"kernel": "decode_split_kernel<PageNv4>", "mean_us": round(sum(kms) / len(kms) * 1e3, 2),
                       "median_us": round(srt[len(srt) // 2] * 1e3, 2), "min_us": round(srt[0] * 1e3, 2),
                       "max_us": round(srt[-1] * 1e3, 2), "samples": len(kms),
-                      "method": "hipEvents (no system fence) recorded by the split kernel's own dispatch, in "
+                      "method": "hipEvents (no system fence) recorded by the kernel's own dispatch, in "
                                 f"{KERNEL_SAMPLES} steps after the timed region; the recording adds a few us"}
-        timed_kernel = ("decode step: decode_split_kernel<PageNv4>" +
-                        (" + merge_splits_kernel" if extra.get("num_splits", 1) > 1 else ""))
+        timed_kernel = "decode step: decode_split_kernel<PageNv4> (split streams merged in-kernel)"
         timing = (f"HIP events on the launch stream around the {args.steps} timed steps, divided by "
                   f"{args.steps}: the step's kernels back to back, nothing else in the region")
     else:
@@ -992,7 +991,7 @@ def main():
     if gscale is not None:
         res["global_scale"] = gscale
     if split_only is not None:
-        res["roofline"]["split_kernel_alone"] = split_only
+        res["roofline"]["kernel_events"] = split_only
     if ceiling is not None:
         res["stream_read_ceiling"] = ceiling
         res["pct_of_stream_read_ceiling"] = round(100.0 * value / ceiling["value"], 2)

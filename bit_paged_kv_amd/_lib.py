@@ -237,7 +237,9 @@ def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, num_s
 
 
 def alloc_decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, num_splits: int, device):
-    """Workspace for decode partials (uninitialised: the kernels write before they read)."""
+    """Workspace for decode partials and arrival words (uninitialised: partials are written before
+    they are read, and arrival words left by any earlier launch or by a fresh allocation are
+    recognised by their generation number)."""
     n = decode_workspace_size(batch, num_q_heads, num_kv_heads, num_splits)
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 

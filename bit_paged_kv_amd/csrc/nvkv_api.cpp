@@ -75,6 +75,9 @@ int decode_args_status(const void* q, const int32_t* page_table, int max_pages_p
           0x7FFFFFFFLL ||
       (long long)num_splits * pages_per_split > 0x7FFFFFFFLL)
     return NVKV_E_UNSUPPORTED;
+  // the kernels address the workspace with 32-bit byte offsets
+  if (nvkv::decode_workspace_bytes(batch, num_q_heads, num_kv_heads, num_splits) > 0x7FFFFFFFull)
+    return NVKV_E_UNSUPPORTED;
   return NVKV_OK;
 }
 
@@ -109,11 +112,24 @@ namespace nvkv {
 
 // Split partials of a multi-split decode: per (query row, split) 128 unnormalised output floats,
 // then per (query row, split) the (max, sum) pair -- the layout the decode kernels use.
-// Partial slots: one per (piece, stream) pair along the unit order, at most pieces + streams - 1.
+// Partial slots: one per (piece, stream) pair along the unit order, at most pieces + streams - 1;
+// then one 64-bit arrival word per stream, 16-byte aligned.
 size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits) {
   if (num_splits <= 1) return 0;
-  const size_t slots = (size_t)num_splits + (size_t)batch * hkv;
-  return slots * (size_t)(hq / hkv) * (kD + 2) * sizeof(float);
+  const size_t streams = (size_t)batch * hkv;
+  const size_t partials = ((size_t)num_splits + streams) * (size_t)(hq / hkv) * (kD + 2) * sizeof(float);
+  return ((partials + 15) & ~size_t(15)) + streams * sizeof(unsigned long long);
+}
+
+// Generation numbers tag the arrival words of each decode launch, so a word written by any earlier
+// launch reads as zero arrivals.  They start from a per-process value and skip 0.
+unsigned next_decode_gen() {
+  static std::atomic<unsigned> counter{static_cast<unsigned>(reinterpret_cast<uintptr_t>(&counter) >> 4) * 2654435761u};
+  unsigned g;
+  do {
+    g = counter.fetch_add(1, std::memory_order_relaxed) + 1u;
+  } while (g == 0);
+  return g;
 }
 
 }  // namespace nvkv
@@ -267,6 +283,7 @@ int nvfp4_paged_decode_attn_timed(const void* q, const uint8_t* k_data, const ui
   a.sm_scale = sm_scale;
   a.pages_per_split = pages_per_split;
   a.num_splits = num_splits;
+  a.gen = nvkv::next_decode_gen();
   a.new_k = new_k;
   a.new_v = new_v;
   a.out = out;
@@ -328,6 +345,7 @@ int fp8_paged_decode_attn(const void* q, const uint8_t* k_cache, const uint8_t* 
   a.sm_scale = sm_scale;
   a.pages_per_split = pages_per_split;
   a.num_splits = num_splits;
+  a.gen = nvkv::next_decode_gen();
   a.out = out;
   a.workspace = workspace;
   return launch_status(nvkv::launch_decode(a, stream));
@@ -372,6 +390,7 @@ int nvkv_decode_layers(const nvkv_layer* layers, int num_layers, const int32_t* 
     a.sm_scale = sm_scale;
     a.pages_per_split = pages_per_split;
     a.num_splits = num_splits;
+    a.gen = nvkv::next_decode_gen();
     a.out = L.out;
     a.workspace = workspace;
     int st = launch_status(nvkv::launch_decode(a, stream));

@@ -5,8 +5,9 @@
 // the fly instead of materialising a dequantized copy.  The Blackwell kernel described there
 // stages tiles in shared memory and converts E2M1 pairs to bf16; this one is designed for gfx950:
 //
-//  * one wavefront owns one (sequence, kv head, split of pages); pages are consumed two at a time
-//    (32 tokens = the K depth of one v_mfma_f32_16x16x32_f16);
+//  * the step's pages are cut into equal pieces, one workgroup of four wavefronts each; a wavefront
+//    owns a quarter of each stream's part of its piece and consumes pages two at a time (32
+//    tokens = the K depth of one v_mfma_f32_16x16x32_f16);
 //  * every lane issues one 16-byte load per page for K and one for V (the in-page byte layout puts
 //    each lane's MFMA operand in 16 contiguous bytes), plus its scale bytes -- no LDS staging;
 //  * E2M1 pairs and E4M3 scale pairs become fp16 with the gfx950 pair converts; e2m1 * scale is
@@ -16,7 +17,8 @@
 //  * the global scales are folded into fp32 factors: g_K into the score scale, g_V into the output;
 //  * online softmax in the exp2 domain with wave butterfly reductions; P enters PV as an fp16
 //    hi + lo pair so that it keeps ~22 significant bits; accumulation is fp32;
-//  * splits write unnormalised partial outputs + (max, sum); a second kernel merges them.
+//  * a stream split over several pieces leaves unnormalised partial outputs + (max, sum); the last
+//    of its pieces to finish merges them, so a decode is a single launch.
 #include <atomic>
 #include <mutex>
 #include <type_traits>
@@ -292,6 +294,87 @@ __device__ __forceinline__ int wave_sum(int v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// ---- merge of a stream's partials, by the last of its pieces to publish ----
+// Workspace of a decode with several pieces: partial outputs [slots][group][128] fp32, (max, sum)
+// pairs [slots][group], slots = num_splits + B * Hkv, then one 64-bit arrival word per stream
+// (generation in the high half, pieces arrived in the low half).
+__device__ __forceinline__ size_t partial_slots(const DecodeArgs& a) { return (size_t)a.num_splits + (size_t)a.batch * a.hkv; }
+__device__ __forceinline__ unsigned long long* arrival_words(const DecodeArgs& a) {
+  const size_t bytes = partial_slots(a) * (a.hq / a.hkv) * (kHeadDim + 2) * sizeof(float);
+  return reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(a.workspace) + ((bytes + 15) & ~size_t(15)));
+}
+
+// Arrival words.  A segment that holds part of a stream reads the stream's word when it starts
+// and, when it ends, counts itself in: if the word it read carries another generation (an earlier
+// launch's, or any value in a fresh workspace), it first tries to replace exactly that value by
+// (generation, 0), then adds one.  The word keeps its old value until some workgroup's exchange
+// succeeds, so the first exchange to reach it succeeds and later ones fail harmlessly; each add
+// follows its own workgroup's exchange to the same word (or a read that already saw this
+// generation), so every add lands on a word of this generation.  Nothing waits on another
+// workgroup.
+__device__ __forceinline__ unsigned long long read_arrival_word(unsigned long long* w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned arrive(unsigned long long* w, unsigned long long seen, unsigned gen) {
+  if ((unsigned)(seen >> 32) != gen)
+    __hip_atomic_compare_exchange_strong(w, &seen, (unsigned long long)gen << 32, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  return (unsigned)__hip_atomic_fetch_add(w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+}
+
+// Device-coherent (sc1) buffer stores and loads of the workspace: they are written through to, and
+// read from, the level every XCD shares, so partials pass between workgroups on different XCDs
+// without a cache-wide writeback or invalidation.  Offsets are bytes from the workspace base (the
+// host keeps the workspace under 2^31 bytes).
+constexpr int kCoherent = 16;   // cache-policy operand of the buffer builtins: sc1 (device scope)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const DecodeArgs& a) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.workspace, 0, 0x7FFFFFFF, kBufferWord3);
+}
+
+__device__ __forceinline__ void merge_one(float2 vc, const f4& oc, float& m, float& den, f4& acc) {
+  if (vc.y > 0.0f) {   // an empty quarter carries no partial output
+    const float m_new = fmaxf(m, vc.x);
+    const float f_old = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
+    const float f_new = __builtin_amdgcn_exp2f(vc.x - m_new);
+    den = den * f_old + vc.y * f_new;
+    acc = acc * f_old + oc * f_new;
+    m = m_new;
+  }
+}
+
+// Log-sum-exp merge of the n partials of stream (b, hk) (pieces first .. first + n - 1, partial
+// slots first + stream ..) into the output rows of its query heads: thread t takes head t / 32,
+// channels 4 (t % 32) .. + 3, sixteen partials per memory round trip.
+__device__ void merge_stream(const DecodeArgs& a, int b, int hk, int first, int n) {
+  constexpr int kBatch = 16;
+  const int group = a.hq / a.hkv;
+  const size_t slots = partial_slots(a);
+  const unsigned ml_base = (unsigned)(slots * group * kHeadDim * sizeof(float));
+  const unsigned slot0 = (unsigned)(first + b * a.hkv + hk);
+  const __amdgpu_buffer_rsrc_t ws = ws_rsrc(a);
+  for (int e = threadIdx.x; e < group * 32; e += 64 * kWaves) {
+    const int j = e >> 5, d = (e & 31) * 4;
+    float m = -INFINITY, den = 0.0f;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < n; i0 += kBatch) {
+      float2 v[kBatch];
+      f4 o[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const unsigned ent = (slot0 + (unsigned)min(i0 + k, n - 1)) * (unsigned)group + (unsigned)j;   // re-reads past n
+        const auto mv = __builtin_amdgcn_raw_buffer_load_b64(ws, ml_base + ent * 8u, 0, kCoherent);
+        const u4v ov = __builtin_amdgcn_raw_buffer_load_b128(ws, (ent * kHeadDim + d) * 4u, 0, kCoherent);
+        v[k] = make_float2(__uint_as_float(mv[0]), __uint_as_float(mv[1]));
+        o[k] = f4{__uint_as_float(ov[0]), __uint_as_float(ov[1]), __uint_as_float(ov[2]), __uint_as_float(ov[3])};
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (i0 + k < n) merge_one(v[k], o[k], m, den, acc);
+    }
+    *reinterpret_cast<f4*>(a.out + ((size_t)b * a.hq + (size_t)hk * group + j) * kHeadDim + d) = acc * (1.0f / den);
+  }
+}
+
 // The step's work is the sequence of units of the streams s = b * Hkv + h in order; stream s owns
 // pages(b) + extra units, extra = kStreamCostPages when the lengths differ (else 0): virtual units
 // at its start that stand for the fixed cost of starting a segment (the page-id and first page
@@ -369,6 +452,10 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
     const int seg_begin = max(u0, r0) - r0, seg_end = min(u1 - r0, n_pages);
     const bool has_pages = seg_begin < seg_end;   // a piece may end inside the virtual units
     if (has_pages) {
+      const bool whole = seg_begin == 0 && seg_end == n_pages;
+      unsigned long long* arrival = arrival_words(a) + (size_t)b * a.hkv + hk;
+      unsigned long long seen = 0;
+      if (!whole && threadIdx.x == 0) seen = read_arrival_word(arrival);   // used only when the segment ends
       // lane-derived values are recomputed for every segment (the lane index is opaque to the
       // compiler), so that none of them is hoisted and kept in a register across the whole piece
       const int lane = opaque_lane_id();
@@ -377,7 +464,6 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
       const bool lo_lane = kPack && col >= 8;          // packed: this column carries the low part of P
       uint32_t* vs_slot = vs_lds[wave];
       const bool head_ok = jh < group;
-      const bool whole = seg_begin == 0 && seg_end == n_pages;
       // each wave takes a contiguous, even-sized quarter of the segment
       const int quarter = (((seg_end - seg_begin + kWaves - 1) / kWaves) + 1) & ~1;
       const int pg_begin = min(seg_end, seg_begin + wave * quarter);
@@ -662,13 +748,35 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
           const size_t e = ((size_t)blockIdx.x + (size_t)b * a.hkv + hk) * group + tj;
           float* part_o = reinterpret_cast<float*>(a.workspace);
           float* part_ml = part_o + slots * group * kHeadDim;
-          float* dst = part_o + e * kHeadDim + td;
-          *reinterpret_cast<f4*>(dst) = f4{co[0], co[1], co[2], co[3]} * a.v_gscale;
-          *reinterpret_cast<f4*>(dst + 4) = f4{co[4], co[5], co[6], co[7]} * a.v_gscale;
-          if (td == 0) *reinterpret_cast<float2*>(part_ml + e * 2) = make_float2(cm, cl);
+          // device-coherent stores: the merging workgroup may run on another XCD
+          const __amdgpu_buffer_rsrc_t ws = ws_rsrc(a);
+          const unsigned off = (unsigned)((e * kHeadDim + td) * sizeof(float));
+          const float g = a.v_gscale;
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u4v{__float_as_uint(co[0] * g), __float_as_uint(co[1] * g), __float_as_uint(co[2] * g), __float_as_uint(co[3] * g)},
+              ws, off, 0, kCoherent);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u4v{__float_as_uint(co[4] * g), __float_as_uint(co[5] * g), __float_as_uint(co[6] * g), __float_as_uint(co[7] * g)},
+              ws, off + 16u, 0, kCoherent);
+          if (td == 0) {
+            typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(u2v{__float_as_uint(cm), __float_as_uint(cl)}, ws,
+                                                  (unsigned)((part_ml - part_o) * sizeof(float) + e * 8), 0, kCoherent);
+          }
         }
       }
-
+      if (!whole) {
+        // ---- the last piece of the stream to publish its partial merges the stream ----
+        __shared__ int merge_here;
+        const int r0 = s_start + extra;                        // unit of the stream's first page
+        const int first = r0 / pp, n_pieces = (r0 + n_pages - 1) / pp - first + 1;
+        // every thread's partial stores have completed (vmcnt 0) before the workgroup counts itself in
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) merge_here = arrive(arrival, seen, a.gen) == (unsigned)n_pieces;
+        __syncthreads();
+        if (merge_here) merge_stream(a, b, hk, first, n_pieces);
+      }
     }
 
     // ---- next stream of the piece ----
@@ -683,94 +791,6 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
     }
     if (has_pages) __syncthreads();   // the combine above has read red_o / red_ml before they are written again
   }
-}
-
-// Log-sum-exp merge of the partials of one (sequence, query head) per block.  The block finds the
-// pieces its stream spans from the sequence lengths (as the split kernel does); a stream inside one
-// piece was written out by the split kernel and the block exits.  Otherwise 8 groups of 32 threads
-// take partials g, g + 8, g + 16, ... with a running maximum (4 channels per thread), and the 8
-// group states are combined through LDS.
-constexpr int kMergeGroups = 8;
-__device__ __forceinline__ void merge_one(float2 vc, const f4& oc, float& m, float& den, f4& acc) {
-  if (vc.y > 0.0f) {   // empty splits carry no partial output
-    const float m_new = fmaxf(m, vc.x);
-    const float f_old = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
-    const float f_new = __builtin_amdgcn_exp2f(vc.x - m_new);
-    den = den * f_old + vc.y * f_new;
-    acc = acc * f_old + oc * f_new;
-    m = m_new;
-  }
-}
-__global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml,
-                                                           const int32_t* __restrict__ seq_lens, int batch, int hq,
-                                                           int hkv, int pieces, int min_pages,
-                                                           float* __restrict__ out) {
-  const int row = (int)blockIdx.x;
-  const int b = row / hq, h = row - b * hq;
-  const int group = hq / hkv, hk = h / group, j = h - hk * group;
-  const int lane = threadIdx.x & 63;
-  // pages of the whole step and of the sequences before b, and the length range (each wave
-  // computes the same values); units as in the split kernel
-  int total = 0, before = 0, lmin = 0x7FFFFFFF, lmax = 0;
-  for (int base = 0; base < batch; base += 64) {
-    const int bl = base + lane;
-    const int len = bl < batch ? seq_lens[bl] : 0;
-    const int pg = bl < batch ? seq_pages(len) : 0;
-    total += wave_sum(pg);
-    before += wave_sum(bl < b ? pg : 0);
-    lmin = min(lmin, wave_min(bl < batch ? len : 0x7FFFFFFF));
-    lmax = max(lmax, wave_max(len));
-  }
-  const int extra = lmin == lmax ? 0 : kStreamCostPages;
-  const int n_pages = seq_pages(seq_lens[b]);
-  const int pp = piece_pages((total + extra * batch) * hkv, pieces, min_pages);
-  const int r0 = ((before + extra * b) * hkv + hk * (n_pages + extra)) + extra;   // first page's unit
-  const int first = r0 / pp;
-  const int n = (r0 + n_pages - 1) / pp - first + 1;   // pieces holding pages of the stream
-  if (n == 1) return;
-  const int g = threadIdx.x >> 5;
-  const int d = (threadIdx.x & 31) * 4;
-  const size_t e0 = ((size_t)first + (size_t)b * hkv + hk) * group + j;   // entry of its first partial
-  const float2* ml = reinterpret_cast<const float2*>(part_ml) + e0;
-  const float* po = part_o + e0 * kHeadDim + d;
-  const size_t stride = group;   // entries between consecutive partials of the stream
-  // the first two partials of every group are read together, at indices clamped into the stream's
-  // (an entry past its count is a re-read and dropped): up to 16 partials, one memory round trip
-  const int i0 = min(g, n - 1), i1 = min(g + kMergeGroups, n - 1);
-  const float2 v0 = ml[i0 * stride], v1 = ml[i1 * stride];
-  const f4 o0 = *reinterpret_cast<const f4*>(po + i0 * stride * kHeadDim);
-  const f4 o1 = *reinterpret_cast<const f4*>(po + i1 * stride * kHeadDim);
-  float m = -INFINITY, den = 0.0f;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (g < n) merge_one(v0, o0, m, den, acc);
-  if (g + kMergeGroups < n) merge_one(v1, o1, m, den, acc);
-  for (int i = g + 2 * kMergeGroups; i < n; i += kMergeGroups)   // more than 16 partials
-    merge_one(ml[i * stride], *reinterpret_cast<const f4*>(po + i * stride * kHeadDim), m, den, acc);
-  __shared__ float g_m[kMergeGroups], g_den[kMergeGroups];
-  __shared__ f4 g_acc[kMergeGroups][32];
-  if ((threadIdx.x & 31) == 0) {
-    g_m[g] = m;
-    g_den[g] = den;
-  }
-  g_acc[g][threadIdx.x & 31] = acc;
-  __syncthreads();
-  if (g != 0) return;
-  float mm = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kMergeGroups; ++i)
-    if (g_den[i] > 0.0f) mm = fmaxf(mm, g_m[i]);
-  float dd = 0.0f;
-  f4 aa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < kMergeGroups; ++i) {
-    if (g_den[i] > 0.0f) {
-      const float w = __builtin_amdgcn_exp2f(g_m[i] - mm);
-      dd += w * g_den[i];
-      aa += w * g_acc[i][threadIdx.x];
-    }
-  }
-  *reinterpret_cast<f4*>(out + (size_t)row * kHeadDim + d) = aa * (1.0f / dd);
 }
 
 // Library-held split partials for callers that cannot allocate: one array per device, reached by
@@ -817,13 +837,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t sta
     else
       hipExtLaunchKernelGGL(decode_split_kernel<PageFp8, false>, grid, block, 0, stream, start, stop, 0, a);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_splits == 1) return e;
-  const size_t slots = (size_t)a.num_splits + (size_t)a.batch * a.hkv;
-  const float* part_o = reinterpret_cast<const float*>(a.workspace);
-  const float* part_ml = part_o + slots * (a.hq / a.hkv) * kHeadDim;
-  hipLaunchKernelGGL(merge_splits_kernel, dim3(a.batch * a.hq), dim3(256), 0, stream, part_o, part_ml, a.seq_lens,
-                     a.batch, a.hq, a.hkv, a.num_splits, a.pages_per_split, a.out);
   return hipGetLastError();
 }
 

@@ -36,7 +36,8 @@ hipError_t launch_extend_attn(const void* q, const int32_t* chunk_offsets, const
                               float* out, hipStream_t stream);
 
 // Decode: the step's pages are cut into num_splits equal pieces, one workgroup of four wavefronts
-// each; streams split over several pieces leave partial softmax states that a second kernel merges.
+// each; a stream split over several pieces leaves partial softmax states that the last of its
+// pieces to finish merges.
 enum CacheFormat { kFmtNvfp4 = 0, kFmtFp8 = 1 };
 
 struct DecodeArgs {
@@ -56,10 +57,13 @@ struct DecodeArgs {
   const void* new_k;          // NVFP4 fused append, or null
   const void* new_v;
   float* out;                 // fp32 [B][Hq][128]
-  void* workspace;            // partials when num_splits > 1
+  void* workspace;            // partials and arrival words when num_splits > 1
+  unsigned gen;               // this launch's generation number (nonzero, distinct per launch)
 };
 
 size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits);
+// A fresh generation number for one decode launch (never 0).
+unsigned next_decode_gen();
 
 // Cost, in pages, that the decode partition charges for each stream of a batch whose lengths
 // differ: the start-up of a segment (two memory round trips and the combine) measured against the

@@ -128,7 +128,9 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
  * takes max(pages_per_split, the even ceiling of the step's cost / num_splits) units.
  * A workgroup walks the streams its piece holds: the four wavefronts split each stream's part
  * and combine in LDS.  A stream that lies in one piece is written out directly.  A stream split
- * over several pieces leaves one partial softmax state per piece, and a second kernel merges them.
+ * over several pieces leaves one partial softmax state per piece.  The last of those pieces to
+ * finish merges them (log-sum-exp), found by an arrival count per stream.  A decode is one
+ * kernel launch.
  * nvkv_plan_decode picks num_splits from host-side hints: two pieces per compute unit (all
  * resident at once), or fewer for a small step so that pieces keep at least 16 pages.
  *   max_seq_len  : the longest sequence (tokens, including an appended token), > 0.
@@ -144,9 +146,13 @@ NVKV_API int nvkv_plan_decode(int batch, int num_kv_heads, int max_seq_len, long
 
 /*
  * Workspace bytes for decode with the given plan: partial states for (num_splits + batch *
- * num_kv_heads) pieces-by-streams of (num_q_heads / num_kv_heads) rows of 130 floats.  The size
- * is 0 when num_splits == 1, because one piece holds every stream whole.  The contents need no
- * initialisation.
+ * num_kv_heads) pieces-by-streams of (num_q_heads / num_kv_heads) rows of 130 floats, then one
+ * 64-bit arrival word per stream.  The size is 0 when num_splits == 1, because one piece holds
+ * every stream whole.  The contents need no initialisation: partials are written before they are
+ * read, and every launch tags the arrival words with its own generation number, so a word left by
+ * another call or plan, or any byte pattern in a fresh allocation, reads as no arrivals.  One
+ * workspace may serve calls of any plan and shape in turn; calls that overlap in time on one
+ * workspace race.
  */
 NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                            int num_splits);
@@ -189,10 +195,10 @@ NVKV_API int nvfp4_paged_decode_attn(const void* q,
 
 /*
  * nvfp4_paged_decode_attn_timed -- nvfp4_paged_decode_attn with a measurement hook: split_start and
- * split_stop (hipEvent_t created by the caller with default flags, or NULL) are recorded by the
- * dispatch of the split kernel itself (an extended launch), so hipEventElapsedTime(split_start,
- * split_stop) is that kernel's execution time and no command is added to the stream.  The merge
- * kernel, when launched, is not inside the pair.  Arguments, results and errors as above.
+ * split_stop (hipEvent_t created by the caller, or NULL) are recorded by the dispatch of the decode
+ * kernel itself (an extended launch), so hipEventElapsedTime(split_start, split_stop) is that
+ * kernel's execution time -- the whole decode, merge included -- and no command is added to the
+ * stream.  Arguments, results and errors as above.
  */
 NVKV_API int nvfp4_paged_decode_attn_timed(const void* q,
                             const uint8_t* k_data, const uint8_t* k_scale,

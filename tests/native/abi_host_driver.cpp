@@ -211,17 +211,26 @@ static void check_decode() {
   n.ns = 4;
   g_launches = 0;
   CHECK(n.run_noalloc() == NVKV_OK && g_launches == 1 && g_last_decode.workspace == g_scratch_anchor);
-  n.b = 64, n.hq = 64, n.hkv = 8, n.ns = 7554;     // (7554 + 512) x 8 x 520 B of partials > 32 MiB
+  n.b = 64, n.hq = 64, n.hkv = 8, n.ns = 7553;     // (7553 + 512) x 8 x 520 B of partials + arrival words > 32 MiB
   g_launches = 0;
   CHECK(n.run_noalloc() == NVKV_E_SCRATCH && g_launches == 0);
-  n.ns = 7553;
+  n.ns = 7552;
   CHECK(n.run_noalloc() == NVKV_OK && g_launches == 1);
   n.q = 0;
   CHECK(n.run_noalloc() == NVKV_E_INVAL);
   CHECK(nvkv_decode_noalloc_max_bytes() == (size_t)32 << 20);
   // workspace sizes
   CHECK(nvkv_decode_workspace_size(4, 64, 8, 128, 1) == 0);
-  CHECK(nvkv_decode_workspace_size(4, 64, 8, 128, 16) == (size_t)(16 + 32) * 8 * 130 * 4);
+  CHECK(nvkv_decode_workspace_size(4, 64, 8, 128, 16) == (size_t)(16 + 32) * 8 * 130 * 4 + 32 * 8);
+  // every launch carries its own nonzero generation number
+  {
+    Dec g1, g2;
+    g1.ns = g2.ns = 4;
+    CHECK(g1.run() == NVKV_OK);
+    const unsigned first = g_last_decode.gen;
+    CHECK(g2.run() == NVKV_OK);
+    CHECK(first != 0 && g_last_decode.gen != 0 && g_last_decode.gen != first);
+  }
   CHECK(nvkv_decode_workspace_size(4, 64, 8, 64, 16) == 0);
   CHECK(nvkv_decode_workspace_size(0, 64, 8, 128, 16) == 0);
 }

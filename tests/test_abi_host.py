@@ -97,8 +97,8 @@ def test_plan_rejects_bad_hints(lib):
 def test_workspace_size(lib):
     assert lib.decode_workspace_size(4, 64, 8, 1) == 0                   # one piece: no partials
     n = lib.decode_workspace_size(4, 64, 8, 16)
-    assert n == (16 + 4 * 8) * 8 * 130 * 4                               # [pieces + streams][group][128 + 2] fp32
-    assert lib.decode_workspace_size(1, 4, 1, 3) == (3 + 1) * 4 * 130 * 4
+    assert n == (16 + 4 * 8) * 8 * 130 * 4 + 4 * 8 * 8                   # [pieces + streams][group][128 + 2] fp32,
+    assert lib.decode_workspace_size(1, 4, 1, 3) == (3 + 1) * 4 * 130 * 4 + 8   # then a 64-bit word per stream
     assert lib._lib.nvkv_decode_workspace_size(4, 64, 8, 64, 16) == 0      # head_dim other than 128
 
 
@@ -160,13 +160,13 @@ def _decode_noalloc(lib, **kw):
     (dict(q=None), INVAL), (dict(kd=None), INVAL), (dict(out=MIS), INVAL), (dict(d=64), UNSUP),
     (dict(hq=64, hkv=2), UNSUP), (dict(gk=float("inf")), INVAL), (dict(sm=0.0), INVAL), (dict(ns=0), INVAL),
     (dict(nk=A), INVAL),
-    # partials beyond the library-held array: (7554 pieces + 512 streams) x 8 heads x 520 B > 32 MiB
-    (dict(b=64, hq=64, hkv=8, ns=7554), SCRATCH),
-    (dict(b=64, hq=64, hkv=8, ns=7554, q=None), INVAL),     # argument errors are reported first
+    # partials beyond the library-held array: (7553 pieces + 512 streams) x 8 heads x 520 B + 4 KiB > 32 MiB
+    (dict(b=64, hq=64, hkv=8, ns=7553), SCRATCH),
+    (dict(b=64, hq=64, hkv=8, ns=7553, q=None), INVAL),     # argument errors are reported first
 ])
 def test_noalloc_decode_validation(lib, kw, want):
     assert lib.decode_noalloc_max_bytes() == 32 << 20
-    assert lib.decode_workspace_size(64, 64, 8, 7553) <= 32 << 20 < lib.decode_workspace_size(64, 64, 8, 7554)
+    assert lib.decode_workspace_size(64, 64, 8, 7552) <= 32 << 20 < lib.decode_workspace_size(64, 64, 8, 7553)
     assert _decode_noalloc(lib, **kw) == want
 
 

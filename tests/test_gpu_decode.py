@@ -104,6 +104,37 @@ def test_decode_page_permutation_invariance(nv):
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("fill", ["random", 0x00, 0xFF])
+def test_decode_workspace_reuse_across_plans(nv, ragged, fill):
+    """One workspace, never cleared, starting from arbitrary bytes, shared by calls with different
+    plans (so each call's partials and arrival words sit where other calls left other data) and by
+    an FP8 decode: every result matches the oracle and repeats bit for bit."""
+    wl, pool, gk, gv, want = ragged
+    pt, sl = H.gpu_tables(wl, DEV)
+    q = wl.q().to(DEV)
+    plans = [nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), 0, p) for p in (2, 6, 4, 2)]
+    plans.append((2, 3))
+    size = max(nv.decode_workspace_size(wl.batch, wl.h_q, wl.h_kv, ns) for _, ns in plans)
+    g = torch.Generator(device="cpu").manual_seed(77)
+    if fill == "random":
+        ws = torch.randint(0, 256, (size,), dtype=torch.uint8, generator=g).to(DEV)
+    else:
+        ws = torch.full((size,), fill, dtype=torch.uint8, device=DEV)
+    first = {}
+    for rep in range(2):
+        for plan in plans:
+            got = nv.nvfp4_decode(q, pool, float(gk), float(gv), pt, sl, wl.sm_scale, plan, wl.h_kv,
+                                  workspace=ws).cpu().numpy()
+            H.assert_attention_close(got, want, f"plan {plan} fill {fill}")
+            if plan in first:
+                assert np.array_equal(got, first[plan])
+            first.setdefault(plan, got)
+        # an FP8 decode of other data through the same workspace in between
+        fp8_pool = nv.alloc_fp8_pool(wl.num_pages, wl.h_kv, DEV, fill=0)
+        nv.fp8_decode(q, fp8_pool, 1.0, 1.0, pt, sl, wl.sm_scale, plans[0], wl.h_kv, workspace=ws)
+    torch.cuda.synchronize()
+
+
 def test_decode_repeat_calls_agree_to_rounding(nv, ragged):
     """Run-to-run: a shared workspace reused by several calls gives the same result each time."""
     wl, pool, gk, gv, want = ragged

@@ -53,7 +53,7 @@ def test_noalloc_rejects_partials_beyond_the_array():
     pool = nv.alloc_nvfp4_pool(1, 8, DEV)
     pt = torch.zeros((64, 1), dtype=torch.int32, device=DEV)
     sl = torch.ones(64, dtype=torch.int32, device=DEV)
-    # (7554 pieces + 512 streams) x 8 heads x 520 B of partials: just past the 32 MiB array
-    assert nv.decode_workspace_size(64, 64, 8, 7553) <= nv.decode_noalloc_max_bytes()
+    # (7553 pieces + 512 streams) x 8 heads x 520 B of partials and 512 arrival words: just past 32 MiB
+    assert nv.decode_workspace_size(64, 64, 8, 7552) <= nv.decode_noalloc_max_bytes()
     with pytest.raises(RuntimeError, match="status -5"):
-        nv.nvfp4_decode_noalloc(q, pool, 1.0, 1.0, pt, sl, 0.1, (2, 7554), 8)
+        nv.nvfp4_decode_noalloc(q, pool, 1.0, 1.0, pt, sl, 0.1, (2, 7553), 8)
