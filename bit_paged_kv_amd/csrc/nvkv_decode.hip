@@ -386,6 +386,33 @@ __device__ __forceinline__ int piece_pages(int total_units, int pieces, int min_
   return max(min_pages, (((total_units + pieces - 1) / pieces) + 1) & ~1);
 }
 
+// Pieces of an equal-length batch come in pairs: workgroups i and i + G/2 of a grid of two per
+// compute unit share a unit, and the older of the two (the first dispatched) is favoured by the
+// wave arbiter, so it finishes first and the younger ends alone.  Pair k (units 2k pp .. 2k pp +
+// 2 pp) is split 9 : 7 -- piece 2k, the older workgroup k's, takes pp + pp / 8 -- which keeps
+// pairs aligned to stream boundaries whenever single pieces were (long contexts, 4 x 131072:
+// 118.4 against 120.0 us per step, side by side).  Pieces are numbered in unit order.
+struct Pieces {
+  int pp;      // units per piece (the pair's mean)
+  int first;   // units of the first piece of a pair (pp unless paired)
+  bool paired;
+  __device__ int start(int piece) const {
+    return paired ? (piece >> 1) * 2 * pp + (piece & 1) * first : piece * pp;
+  }
+  __device__ int of(int u) const {   // the piece holding unit u
+    if (!paired) return u / pp;
+    const int k = u / (2 * pp);
+    return 2 * k + (u - k * 2 * pp >= first ? 1 : 0);
+  }
+};
+__device__ __forceinline__ Pieces make_pieces(int units, int pieces, int min_pages, bool equal_lengths) {
+  Pieces p;
+  p.pp = piece_pages(units, pieces, min_pages);
+  p.paired = equal_lengths && pieces >= 2 && (pieces & 1) == 0;
+  p.first = p.paired ? (p.pp + p.pp / 8) & ~1 : p.pp;
+  return p;
+}
+
 // One workgroup of four waves per piece.  A piece is walked as segments (the pages of one stream
 // it holds); each wave takes a contiguous, even-sized quarter of a segment and the four combine in
 // LDS.  A segment holding a whole stream writes the normalised output; the others write their
@@ -415,10 +442,13 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
   }
   const int extra = lmin == lmax ? 0 : kStreamCostPages;
   const int units = (total + extra * a.batch) * a.hkv;
-  const int pp = piece_pages(units, (int)gridDim.x, a.pages_per_split);
-  int u0 = (int)blockIdx.x * pp;
+  const Pieces pcs = make_pieces(units, (int)gridDim.x, a.pages_per_split, extra == 0);
+  const int half = (int)gridDim.x / 2;
+  const int piece = !pcs.paired ? (int)blockIdx.x
+                                : (int)blockIdx.x < half ? 2 * (int)blockIdx.x : 2 * ((int)blockIdx.x - half) + 1;
+  int u0 = pcs.start(piece);
   if (u0 >= units) return;
-  const int u1 = min(units, u0 + pp);
+  const int u1 = min(units, pcs.start(piece + 1));
   // the sequence holding unit u0: the first with Hkv * (cost up to and including it) > u0
   int base = 0, before = 0;   // before: cost of the sequences before `base`
   if (a.batch > 64) {
@@ -745,7 +775,7 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
           *reinterpret_cast<f4*>(dst + 4) = f4{co[4], co[5], co[6], co[7]} * f;
         } else {
           const size_t slots = (size_t)a.num_splits + (size_t)a.batch * a.hkv;
-          const size_t e = ((size_t)blockIdx.x + (size_t)b * a.hkv + hk) * group + tj;
+          const size_t e = ((size_t)piece + (size_t)b * a.hkv + hk) * group + tj;
           float* part_o = reinterpret_cast<float*>(a.workspace);
           float* part_ml = part_o + slots * group * kHeadDim;
           // device-coherent stores: the merging workgroup may run on another XCD
@@ -769,7 +799,7 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
         // ---- the last piece of the stream to publish its partial merges the stream ----
         __shared__ int merge_here;
         const int r0 = s_start + extra;                        // unit of the stream's first page
-        const int first = r0 / pp, n_pieces = (r0 + n_pages - 1) / pp - first + 1;
+        const int first = pcs.of(r0), n_pieces = pcs.of(r0 + n_pages - 1) - first + 1;
         // every thread's partial stores have completed (vmcnt 0) before the workgroup counts itself in
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
