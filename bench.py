@@ -132,8 +132,8 @@ def host_cpu():
 # (the decode file and the headers it includes, hashed together) and the split plan they were taken
 # with; reported as null otherwise.
 TRAFFIC = {
-    "long": {"source_sha256": "1e4675a0642f3f7ff8a90d4104802a32bfa8adc858865d2e02cb41fadd9019e7", "plan": [512, 16],
-             "kernels": {"decode_split_kernel": (296026.5, 2203.1), "merge_splits_kernel": (1063.0, 128.0)},
+    "long": {"source_sha256": "9e98f3dd5ce9f6eed155599dcc6b6578d8ed23dccbc025914b6b0bda36e84056", "plan": [2, 512],
+             "kernels": {"decode_split_kernel": (296438.3, 4304.0)},
              "fetch_factor": 2.0, "write_factor": 1.0},
 }
 
