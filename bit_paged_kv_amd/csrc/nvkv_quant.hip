@@ -117,6 +117,7 @@ constexpr int kQTok = NVKV_Q_TOKENS;      // tokens a workgroup quantizes (a pow
 constexpr int kQWin = kQTok - 3;          // tokens it owns; the last three are the halo
 constexpr int kQItems = kQTok * 16;       // (token, block, K|V) items of phase 1
 constexpr int kQThreads = NVKV_Q_THREADS;
+static_assert(kQWin <= 64, "the V writers of a window are listed by one wave");
 
 // kWs: the prefill write -- every owned token's K and V also go, as E4M3 of fp32(x / s_ws) (the FP8
 // encoding of the mixed-precision layers), to row t of a dense FP8 copy [n_tok][hkv][128] that the
@@ -130,6 +131,8 @@ __global__ __launch_bounds__(kQThreads) void nvfp4_quantize_kernel(
   __shared__ uint2 vcodes[kQTok][8];      // [token in window][block]: element i at bits 4 (i % 8) of word i / 8
   __shared__ uint8_t vscales[kQTok][8];
   __shared__ int32_t wslots[kQTok + 3];   // slots of input tokens w0 - 3 .. w0 + kQTok - 1 (-1: none)
+  __shared__ int8_t vlist[kQWin];         // owned tokens that write V: quad leaders first, then lone tokens
+  __shared__ int vcount[2];               // number of leaders, number of lone tokens
   const int h = blockIdx.y;
   const int w0 = blockIdx.x * kQWin;
   if (threadIdx.x < kQTok + 3) {
@@ -164,6 +167,7 @@ __global__ __launch_bounds__(kQThreads) void nvfp4_quantize_kernel(
       vcodes[tr][j] = make_uint2(lo, hi);
       vscales[tr][j] = (uint8_t)sc;
     } else {
+      // from global memory: wslots is not complete before the barrier that ends this phase
       const int slot = slots[t];
       const int o = slot & 15;
       const size_t blk = (size_t)(slot >> 4) * hkv + h;
@@ -174,25 +178,45 @@ __global__ __launch_bounds__(kQThreads) void nvfp4_quantize_kernel(
     }
   }
   __syncthreads();
-  // phase 2: V of the owned tokens, one thread per (token, block)
+  // V writers of the window: an owned token is the leader of a complete quad (its slot starts an
+  // aligned quad whose four slots are taken by it and the next three input tokens), inside one
+  // (written by its leader, here or in the previous window, whose halo holds it), or lone.  The
+  // first wave lists the leaders, then the lone tokens, so that phase 2 runs one thread per
+  // (writer, block) with no idle lanes between them.
+  if (threadIdx.x < 64) {
+    const int tr = (int)threadIdx.x, t = w0 + tr;
+    bool leader = false, lone = false;
+    if (tr < kQWin && t < n_tok) {
+      const int slot = wslots[tr + 3], r = slot & 3;
+      // the quad is complete if input tokens t - r .. t - r + 3 hold exactly slots slot - r .. slot - r + 3
+      // (wslots index of token t - r + m: tr + 3 - r + m, within 0 .. kQTok + 2)
+      bool complete = t - r >= 0 && t - r + 3 < n_tok;
 #pragma unroll
-  for (int it = 0; it < (kQWin * 8 + kQThreads - 1) / kQThreads; ++it) {
-    const int task = it * kQThreads + (int)threadIdx.x;
-    const int tr = task >> 3, j = task & 7;
-    const int t = w0 + tr;
-    if (tr >= kQWin || t >= n_tok) continue;
+      for (int m = 0; m < 4; ++m) complete = complete && (m == r || wslots[tr + 3 - r + m] == slot - r + m);
+      leader = complete && r == 0;
+      lone = !complete;
+    }
+    const unsigned long long lm = __ballot(leader), am = __ballot(lone);
+    const unsigned long long below = (1ull << tr) - 1ull;
+    const int nl = __popcll(lm);
+    if (leader) vlist[__popcll(lm & below)] = (int8_t)tr;
+    if (lone) vlist[nl + __popcll(am & below)] = (int8_t)tr;
+    if (tr == 0) {
+      vcount[0] = nl;
+      vcount[1] = __popcll(am);
+    }
+  }
+  __syncthreads();
+  // phase 2: V of the listed tokens, one thread per (writer, block)
+  const int n_lead = vcount[0], n_writers = vcount[0] + vcount[1];
+  for (int task = (int)threadIdx.x; task < n_writers * 8; task += kQThreads) {
+    const int idx = task >> 3, j = task & 7;
+    const int tr = vlist[idx];
     const int slot = wslots[tr + 3];
-    const int o = slot & 15, r = slot & 3;
+    const int o = slot & 15;
     const size_t blk = (size_t)(slot >> 4) * hkv + h;
-    // the quad of aligned slots slot - r .. slot - r + 3 is complete if input tokens t - r .. t - r + 3
-    // hold exactly those slots (wslots index of token t - r + m: tr + 3 - r + m, within 0 .. kQTok + 2)
-    const int lead = t - r;
-    bool complete = lead >= 0 && lead + 3 < n_tok;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) complete = complete && (m == r || wslots[tr + 3 - r + m] == slot - r + m);
-    if (complete && r != 0) continue;     // written by its leader
     uint8_t* vd = v_data + blk * kNvfp4DataBytes;
-    if (complete) {
+    if (idx < n_lead) {
       // 4x16 nibble transpose: word of channel i = nibbles of tokens 0..3 at bits 0, 4, 8, 12
       const uint2 c0 = vcodes[tr][j], c1 = vcodes[tr + 1][j], c2 = vcodes[tr + 2][j], c3 = vcodes[tr + 3][j];
       uint8_t* base = vd + (o >> 2) * 256 + 2 * j;
