@@ -108,7 +108,7 @@ __device__ __forceinline__ void load_block16(const uint8_t* base, int in_dtype, 
 // stores except at run ends.
 // ---------------------------------------------------------------------------------------------
 #ifndef NVKV_Q_TOKENS
-#define NVKV_Q_TOKENS 32
+#define NVKV_Q_TOKENS 64
 #endif
 #ifndef NVKV_Q_THREADS
 #define NVKV_Q_THREADS 512
