@@ -104,6 +104,28 @@ def test_decode_page_permutation_invariance(nv):
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("lens_kind", ["ragged", "equal"])
+def test_decode_batch_over_64(nv, lens_kind):
+    """More than 64 sequences: every workgroup finds its first stream, and the merging piece its
+    stream's pieces, from the lengths 64 at a time.  Ragged lengths (pieces of equal cost, several
+    streams per piece) and equal ones (paired pieces), under the automatic plan and forced ones."""
+    rng = np.random.default_rng(130)
+    lens = rng.integers(1, 200, size=130) if lens_kind == "ragged" else np.full(130, 70)
+    wl = workloads.Workload(name=f"b130-{lens_kind}", seed=131, batch=130, h_kv=2, h_q=8,
+                            seq_lens=[int(x) for x in lens], extra_pages=9)
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    want = H.oracle_nvfp4_decode(wl, wl.q().float().numpy(), ks, vs, gk, gv)
+    pool, _, _ = H.gpu_nvfp4_layer(wl, 0, DEV, fill=0xFF)
+    outs = []
+    for pps in (0, 2, 6, 1000):
+        got, plan = _run_nvfp4(nv, wl, pool, float(gk), float(gv), force_pps=pps)
+        H.assert_attention_close(got, want, f"{lens_kind} plan={plan}")
+        outs.append(got)
+    for o in outs[1:]:   # plans differ only in the order of fp32 sums
+        np.testing.assert_allclose(o, outs[0], rtol=1e-5, atol=1e-5)
+
+
 @pytest.mark.parametrize("fill", ["random", 0x00, 0xFF])
 def test_decode_workspace_reuse_across_plans(nv, ragged, fill):
     """One workspace, never cleared, starting from arbitrary bytes, shared by calls with different
