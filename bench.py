@@ -629,7 +629,8 @@ def main():
         kernel_bytes = step_bytes
         desc = (f"{name}: batch {wl.batch}, context {int(wl.seq_lens[0]) if name != 'ragged' else 'ragged'}, "
                 f"{wl.h_kv} KV / {wl.h_q} query heads, head_dim 128, page 16, NVFP4 cache, "
-                f"{plan[1]} equal pieces (at least {plan[0]} pages), split streams merged in-kernel")
+                f"{plan[1]} pieces of equal cost (at least {plan[0]} pages; paired 9:7 per compute unit when the "
+                f"lengths are equal), split streams merged in-kernel")
         extra = {"batch": wl.batch, "context_tokens": int(wl.total_lens.sum()), "kv_heads": wl.h_kv,
                  "q_heads": wl.h_q, "head_dim": 128, "page_size": 16, "cache": "nvfp4",
                  "pages_per_split": plan[0], "num_splits": plan[1], "cache_copies_rotated": copies,
