@@ -132,8 +132,8 @@ def host_cpu():
 # (the decode file and the headers it includes, hashed together) and the split plan they were taken
 # with; reported as null otherwise.
 TRAFFIC = {
-    "long": {"source_sha256": "9e98f3dd5ce9f6eed155599dcc6b6578d8ed23dccbc025914b6b0bda36e84056", "plan": [2, 512],
-             "kernels": {"decode_split_kernel": (296438.3, 4304.0)},
+    "long": {"source_sha256": "76fa8448de4f61cd3242603923fba49af887d674d5925c0c7123ea52db3ad908", "plan": [2, 512],
+             "kernels": {"decode_split_kernel": (296439.2, 4304.0)},
              "fetch_factor": 2.0, "write_factor": 1.0},
 }
 

@@ -31,7 +31,7 @@
 
 namespace nvkv {
 
-constexpr int kWaves = 4;  // independent splits per workgroup
+constexpr int kWaves = 4;  // waves per workgroup, each on a quarter of a segment
 
 template <int I, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -332,7 +332,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const DecodeArgs& a) {
 }
 
 __device__ __forceinline__ void merge_one(float2 vc, const f4& oc, float& m, float& den, f4& acc) {
-  if (vc.y > 0.0f) {   // an empty quarter carries no partial output
+  if (vc.y > 0.0f) {   // a partial of zero weight contributes nothing
     const float m_new = fmaxf(m, vc.x);
     const float f_old = __builtin_amdgcn_exp2f(m - m_new);   // 0 while m is -inf
     const float f_new = __builtin_amdgcn_exp2f(vc.x - m_new);
@@ -417,9 +417,10 @@ __device__ __forceinline__ Pieces make_pieces(int units, int pieces, int min_pag
 // it holds); each wave takes a contiguous, even-sized quarter of a segment and the four combine in
 // LDS.  A segment holding a whole stream writes the normalised output; the others write their
 // unnormalised partial output (times g_V) and (max, sum) in log2 units at partial slot
-// (piece + stream) -- unique, since both grow along the unit order -- for the merge kernel.
-// Workspace: partial outputs [num_splits + B * Hkv][group][128], then (max, sum) pairs
-// [num_splits + B * Hkv][group]; every entry read is written first, so it needs no initialisation.
+// (piece + stream) -- unique, since both grow along the unit order -- and count themselves in on
+// the stream's arrival word; the last of a stream's pieces merges its partials (merge_stream).
+// Partials are written before they are read and arrival words carry the launch's generation, so
+// the workspace needs no initialisation.
 //
 // kPack (query heads per kv head <= 8): score columns 8..15 repeat heads 0..7, and those lanes feed
 // the low fp16 part of P into the PV product while columns 0..7 feed the high part, so one MFMA per
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
 
       float m_run = -INFINITY, l_run = 0.0f;
       f4 o[8];
-    #pragma unroll
+#pragma unroll
       for (int n = 0; n < 8; ++n) o[n] = f4{0.f, 0.f, 0.f, 0.f};
 
       if (pg_begin < pg_end) {
@@ -530,17 +531,17 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
         auto load_q = [&] {
           const uint4* qp =
               reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + row * kHeadDim + 32 * c);
-    #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) q_raw[i] = qp[i];
         };
         auto prep_q = [&] {
           float qf[32];
-    #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) bf16x8_to_f32(q_raw[i], qf + 8 * i);
-    #pragma unroll
+#pragma unroll
           for (int i = 0; i < 32; ++i) qf[i] = head_ok ? qf[i] : 0.0f;
           float qmax = 0.0f;
-    #pragma unroll
+#pragma unroll
           for (int i = 0; i < 32; ++i) qmax = fmaxf(qmax, fabsf(qf[i]));
           qmax = max_xor16(qmax);
           qmax = max_xor32(qmax);
@@ -550,9 +551,9 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
             (void)frexpf(qmax, &ex);          // qmax = f * 2^ex, f in [0.5, 1)
             qexp = min(max(14 - ex, -100), 100);
           }
-    #pragma unroll
+#pragma unroll
           for (int s = 0; s < 4; ++s)
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 8; ++i) qb[s][i] = (_Float16)__builtin_ldexpf(qf[8 * s + i], qexp);
           // scores in log2 units: <q, K_hat> * sm_scale * log2(e); K_hat = (e2m1 * s_blk) * g_K
           qk_scale = a.sm_scale * 1.44269504088896341f * a.k_gscale * __builtin_ldexpf(1.0f, -qexp);
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
           s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<2>(p1, sc1), qb[2], s1, 0, 0, 0);
           s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p0, sc0), qb[3], s0, 0, 0, 0);
           s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_operand<3>(p1, sc1), qb[3], s1, 0, 0, 0);
-    #pragma unroll
+#pragma unroll
           for (int r = 0; r < 4; ++r) {
             x[r] = s0[r];
             x[4 + r] = s1[r];
@@ -609,7 +610,7 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
           if (tail) {
             asm volatile("" ::: "memory");
             const int t0 = 4 * (opaque_lane_id() >> 4);   // first token row of this lane
-    #pragma unroll
+#pragma unroll
             for (int r = 0; r < 4; ++r) {
               if (t0 + r >= nv0) x[r] = -INFINITY;
               if (t0 + r >= nv1) x[4 + r] = -INFINITY;
@@ -629,25 +630,25 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
             const float m_new = fmaxf(m_run, hmax * qk_scale);   // qk_scale > 0: the max commutes with it
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
-    #pragma unroll
+#pragma unroll
             for (int n = 0; n < 8; ++n) o[n] *= alpha;
             m_run = m_new;
             thr = (m_run + kSlack) / qk_scale;
           }
           float pr[8];
-    #pragma unroll
+#pragma unroll
           for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], qk_scale, -m_run));
           l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
           // P = hi + lo in fp16: hi rounds toward zero, lo = fp16(P - hi) keeps ~11 more bits
           h2 ph2[4], pl2[4];
-    #pragma unroll
+#pragma unroll
           for (int k = 0; k < 4; ++k) {
             ph2[k] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2 * k], pr[2 * k + 1]));
             pl2[k] = lo_part(pr[2 * k], pr[2 * k + 1], ph2[k]);
           }
           if constexpr (kPack) {
             h2 pp[4];
-    #pragma unroll
+#pragma unroll
             for (int k = 0; k < 4; ++k) pp[k] = lo_lane ? pl2[k] : ph2[k];
             const h8 pb = cat4(pp[0], pp[1], pp[2], pp[3]);
             static_for<0, 8>([&](auto nc) {
@@ -731,16 +732,16 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
         __builtin_amdgcn_s_setprio(0);
         l_run = sum_xor32(sum_xor16(l_run));
         if constexpr (kPack) {
-    #pragma unroll
+#pragma unroll
           for (int n = 0; n < 8; ++n)
-    #pragma unroll
+#pragma unroll
             for (int r = 0; r < 4; ++r) o[n][r] += from_lane_xor8(o[n][r]);
         }
       }
 
       // ---- combine the 4 waves of this workgroup (lane holds O^T[16n + 4c + r][head jh]) ----
       if (!lo_lane) {
-    #pragma unroll
+#pragma unroll
         for (int n = 0; n < 8; ++n) *reinterpret_cast<f4*>(&red_o[wave][jh][16 * n + 4 * c]) = o[n];
         if (c == 0) {
           red_ml[wave][jh][0] = m_run;
@@ -753,18 +754,18 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
       const int td = (tid & 15) * 8;              // first of its 8 channels
       if (tj < group) {
         float cm = -INFINITY, cl = 0.0f, co[8];
-    #pragma unroll
+#pragma unroll
         for (int w = 0; w < kWaves; ++w)
           if (red_ml[w][tj][1] > 0.0f) cm = fmaxf(cm, red_ml[w][tj][0]);
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8; ++i) co[i] = 0.0f;
-    #pragma unroll
+#pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           const float lw = red_ml[w][tj][1];
           if (lw > 0.0f) {
             const float wt = __builtin_amdgcn_exp2f(red_ml[w][tj][0] - cm);
             cl += wt * lw;
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 8; ++i) co[i] += wt * red_o[w][tj][td + i];
           }
         }
@@ -774,7 +775,7 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
           *reinterpret_cast<f4*>(dst) = f4{co[0], co[1], co[2], co[3]} * f;
           *reinterpret_cast<f4*>(dst + 4) = f4{co[4], co[5], co[6], co[7]} * f;
         } else {
-          const size_t slots = (size_t)a.num_splits + (size_t)a.batch * a.hkv;
+          const size_t slots = partial_slots(a);
           const size_t e = ((size_t)piece + (size_t)b * a.hkv + hk) * group + tj;
           float* part_o = reinterpret_cast<float*>(a.workspace);
           float* part_ml = part_o + slots * group * kHeadDim;
@@ -823,10 +824,11 @@ __global__ __launch_bounds__(64 * kWaves, 3) void decode_split_kernel(DecodeArgs
   }
 }
 
-// Library-held split partials for callers that cannot allocate: one array per device, reached by
-// the kernels only through the device address hipGetSymbolAddress returns (the array's name is a
-// host-side stand-in in this code).  The partials are written before they are read, so the array
-// needs no clearing; calls that overlap on one device share it and race.
+// Library-held split partials and arrival words for callers that cannot allocate: one array per
+// device, reached by the kernels only through the device address hipGetSymbolAddress returns (the
+// array's name is a host-side stand-in in this code).  The partials are written before they are
+// read and the arrival words carry each launch's generation, so the array needs no clearing; calls
+// that overlap on one device share it and race.
 static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 
 hipError_t decode_scratch(void** ptr) {
