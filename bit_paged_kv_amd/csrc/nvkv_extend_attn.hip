@@ -260,10 +260,10 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
     }
   };
 
-  // matrix phase: S(tile) = K Q^T, then O += V P for tile - 1 (kPV false for tile 0).  All 16
-  // operand reads are issued before the products, so LDS latency is paid about once per phase
-  // instead of once per few products.  (Pinning the instruction order further, or keeping the
-  // products ahead of the phase-ending barrier, measured slower.)
+  // matrix phase: S(tile) = K Q^T, then O += V P for tile - 1 (kPV false for tile 0).  The compiler
+  // issues the 16 operand reads two at a time, each pair just ahead of the products that use it;
+  // pinning another order (all reads first, or reads interleaved with the QK products), or keeping
+  // the products ahead of the phase-ending barrier, measured slower.
   auto matrix_phase = [&](int tile, auto pv_tag) {
     constexpr bool kPV = decltype(pv_tag)::value;
     if constexpr (kPV) apply_rescale();   // O is not read by the QK products: rescaling first is exact
