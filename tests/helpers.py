@@ -5,6 +5,9 @@ C-ABI binding.  Nothing computed by the GPU is ever fed to the oracle.
 """
 from __future__ import annotations
 
+import hashlib
+import os
+
 import numpy as np
 import torch
 
@@ -113,3 +116,67 @@ def gpu_tables(wl, dev, seq_lens=None):
 
 def pool_to_numpy(pool):
     return {k: t.cpu().numpy() for k, t in pool.items()}
+
+
+# ------------------------------------------------------------------------------------------------
+# whole full-size caches: every stream's code and scale bytes, compared through digests
+# ------------------------------------------------------------------------------------------------
+def host_workers() -> int:
+    """Worker processes for oracle work on the host: the cores this process may use, at most 16
+    (the host-CPU share of one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def stream_digest(*arrays) -> str:
+    """sha256 over one (sequence, kv head) stream's bytes, each array as contiguous uint8 in token
+    order: NVFP4 K codes [n][128], K scale bytes [n][8], V codes, V scale bytes; or FP8 K and V
+    bytes [n][128]."""
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a, dtype=np.uint8).tobytes())
+    return h.hexdigest()
+
+
+def oracle_stream_digests(task) -> dict:
+    """Host worker: digests of the oracle's cache bytes for the streams (b, hk), hk in `heads`, of a
+    workload (a config index or a Workload) and layer, from its seeded inputs alone (the appended
+    token included when the workload appends), under the oracle's scales s_k, s_v: NVFP4 global
+    scales, or FP8 per-tensor scales when `fp8`.  task = (which, b, heads, s_k, s_v[, layer, fp8])."""
+    which, b, heads, s_k, s_v, layer, fp8 = (tuple(task) + (0, False))[:7]
+    wl = workloads.config(which) if isinstance(which, int) else which
+    k, v = wl.kv("k", b, layer), wl.kv("v", b, layer)
+    nk = wl.new_token("k", layer)[b] if wl.append else None
+    nv = wl.new_token("v", layer)[b] if wl.append else None
+    out = {}
+    for hk in heads:
+        kh, vh = k[:, hk].float().numpy(), v[:, hk].float().numpy()
+        if wl.append:
+            kh = np.concatenate([kh, nk[hk][None].float().numpy()])
+            vh = np.concatenate([vh, nv[hk][None].float().numpy()])
+        if fp8:
+            out[(b, hk)] = stream_digest(o_fp8.fp8_quantize(kh, s_k), o_fp8.fp8_quantize(vh, s_v))
+        else:
+            ck, sk = o_nv.quantize_blocks(kh, s_k)
+            cv, sv = o_nv.quantize_blocks(vh, s_v)
+            out[(b, hk)] = stream_digest(ck, sk, cv, sv)
+    return out
+
+
+def digest_tasks(wl, which, s_k, s_v, layer=0, fp8=False) -> list:
+    """oracle_stream_digests tasks covering every stream of a workload: one per sequence, or per
+    pair of kv heads for sequences long enough to keep a worker busy on their own."""
+    return [(which, b, heads, s_k, s_v, layer, fp8) for b in range(wl.batch)
+            for heads in ([list(range(wl.h_kv))] if wl.seq_lens[b] <= 32768 else
+                          [[h, h + 1] for h in range(0, wl.h_kv, 2)])]
+
+
+def pool_stream_digest(rows, n_tok: int, fp8: bool = False) -> str:
+    """Digest of one stream's bytes as a GPU pool holds them: `rows` is {key: [pages][1][bytes]}
+    of the stream's pages in sequence order (token t at local slot t)."""
+    local = np.arange(n_tok)
+    if fp8:
+        return stream_digest(o_layout.read_fp8_tokens(rows["k"], "k", local)[:, 0],
+                             o_layout.read_fp8_tokens(rows["v"], "v", local)[:, 0])
+    ck, sk = o_layout.read_nvfp4_tokens(rows["k_data"], rows["k_scale"], "k", local)
+    cv, sv = o_layout.read_nvfp4_tokens(rows["v_data"], rows["v_scale"], "v", local)
+    return stream_digest(ck[:, 0], sk[:, 0], cv[:, 0], sv[:, 0])

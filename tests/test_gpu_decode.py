@@ -1,5 +1,7 @@
 """GPU parity of decode attention through the C ABI against the fp64 oracle on the oracle's own
 dequantized cache: max-abs <= 2e-3 and rel-L2 <= 1e-3 over the whole output (tests/helpers.py)."""
+import multiprocessing as mp
+
 import numpy as np
 import pytest
 import torch
@@ -309,8 +311,10 @@ def _assert_nvfp4_rows(rows, ck, sk, cv, sv, tag):
 
 
 def _sampled_full_size(nv, index, samples):
-    """Full-size workload in the bench's launch configuration; the oracle recomputes the sampled
-    (sequence, kv head) rows from the same seeded inputs (never from anything the GPU produced)."""
+    """Full-size workload in the bench's launch configuration.  Every (sequence, kv head) stream's
+    code and scale bytes, as the step left them, are compared with the oracle's (digests that a
+    pool of host workers computes from the seeded inputs); the oracle recomputes the sampled
+    streams' attention rows from the same inputs.  Nothing the GPU produced is fed to the oracle."""
     wl = workloads.config(index)
     ks = [wl.kv("k", b) for b in range(wl.batch)]
     vs = [wl.kv("v", b) for b in range(wl.batch)]
@@ -329,15 +333,32 @@ def _sampled_full_size(nv, index, samples):
     nvv = wl.new_token("v") if fused else None
     out = nv.nvfp4_decode(q.to(DEV), pool, gk, gv, pt, sl, wl.sm_scale, plan, wl.h_kv,
                           new_k=nk.to(DEV) if fused else None, new_v=nvv.to(DEV) if fused else None).cpu().numpy()
-    # the sampled streams' pages as the step left them (the appended token included)
-    rows = {(b, hk): _pool_rows(pool, wl, b, hk, int(wl.total_lens[b])) for b, hk in samples}
-    del pool
-    torch.cuda.empty_cache()
     print(f"cfg{index}: GPU step done, plan {plan}", flush=True)
     # the oracle's own global scales, over the whole cached tensors
     ogk = o_nv.global_scale(np.array([max(float(t.float().abs().max()) for t in ks)], np.float32))
     ogv = o_nv.global_scale(np.array([max(float(t.float().abs().max()) for t in vs)], np.float32))
     assert (np.float32(gk), np.float32(gv)) == (ogk, ogv)
+    # every stream's pages as the step left them (the appended token included), digested here
+    # while host workers digest the oracle's bytes of the same streams
+    rows, got = {}, {}
+    with mp.get_context("spawn").Pool(H.host_workers()) as workers:
+        pending = workers.map_async(H.oracle_stream_digests, H.digest_tasks(wl, index, ogk, ogv))
+        for b in range(wl.batch):
+            n_tok = int(wl.total_lens[b])
+            for hk in range(wl.h_kv):
+                r = _pool_rows(pool, wl, b, hk, n_tok)
+                got[(b, hk)] = H.pool_stream_digest(r, n_tok)
+                if (b, hk) in samples:
+                    rows[(b, hk)] = r
+        want = {}
+        for d in pending.get(timeout=600):
+            want.update(d)
+    del pool
+    torch.cuda.empty_cache()
+    bad = sorted(s for s in got if got[s] != want.get(s))
+    assert not bad and len(want) == len(got), \
+        f"cfg{index}: {len(bad)} of {len(got)} streams' bytes differ from the oracle's, first (b, hk) {bad[:4]}"
+    print(f"cfg{index}: every code and scale byte of all {len(got)} streams bit-exact", flush=True)
     qf = q.float().numpy()
     G = wl.group
     for b, hk in samples:
@@ -407,8 +428,37 @@ def test_full_size_mixed_stack_sampled(nv):
     outs = [o.cpu().numpy() for o in nv.decode_layers(layers, pt, sl, wl.sm_scale, plan, wl.h_kv)]
     print(f"mixed full size: GPU step done, plan {plan}", flush=True)
     samples = [(0, 0), (21, 5), (43, 7)]
-    rows = {(i, b, hk): _pool_rows(L["pool"], wl, b, hk, int(wl.total_lens[b]))
-            for i, L in enumerate(layers) for b, hk in samples}
+    # the oracle's scales from the seeded inputs; then every stream's bytes of both layers against
+    # the oracle's (digests from host workers), keeping the sampled streams' pages
+    scales = {}
+    for layer in (fp8_layer, nv4_layer):
+        ks, vs, amax_k, amax_v, s1, s2 = host[layer]
+        if wl.is_fp8(layer):
+            scales[layer] = (o_fp8.fp8_scale(amax_k), o_fp8.fp8_scale(amax_v))
+        else:
+            scales[layer] = (o_nv.global_scale(amax_k), o_nv.global_scale(amax_v))
+        assert (np.float32(s1), np.float32(s2)) == scales[layer], f"layer {layer} scales"
+    rows = {}
+    with mp.get_context("spawn").Pool(H.host_workers()) as workers:
+        pending = {layer: workers.map_async(H.oracle_stream_digests,
+                                            H.digest_tasks(wl, 4, *scales[layer], layer, wl.is_fp8(layer)))
+                   for layer in (fp8_layer, nv4_layer)}
+        for i, layer in enumerate((fp8_layer, nv4_layer)):
+            got = {}
+            for b in range(wl.batch):
+                n_tok = int(wl.total_lens[b])
+                for hk in range(wl.h_kv):
+                    r = _pool_rows(layers[i]["pool"], wl, b, hk, n_tok)
+                    got[(b, hk)] = H.pool_stream_digest(r, n_tok, wl.is_fp8(layer))
+                    if (b, hk) in samples:
+                        rows[(i, b, hk)] = r
+            want = {}
+            for d in pending[layer].get(timeout=600):
+                want.update(d)
+            bad = sorted(s for s in got if got[s] != want.get(s))
+            assert not bad and len(want) == len(got), \
+                f"mixed layer {layer}: {len(bad)} of {len(got)} streams' bytes differ, first (b, hk) {bad[:4]}"
+            print(f"mixed full size: layer {layer}: every cache byte of all {len(got)} streams bit-exact", flush=True)
     del layers
     torch.cuda.empty_cache()
     G = wl.group
@@ -416,11 +466,7 @@ def test_full_size_mixed_stack_sampled(nv):
         ks, vs, amax_k, amax_v, s1, s2 = host[layer]
         qf = wl.q(layer).float().numpy()
         fp8 = wl.is_fp8(layer)
-        if fp8:
-            ok, ov = o_fp8.fp8_scale(amax_k), o_fp8.fp8_scale(amax_v)
-        else:
-            ok, ov = o_nv.global_scale(amax_k), o_nv.global_scale(amax_v)
-        assert (np.float32(s1), np.float32(s2)) == (ok, ov), f"layer {layer} scales"
+        ok, ov = scales[layer]
         for b, hk in samples:
             k = ks[b][:, hk].float().numpy()
             v = vs[b][:, hk].float().numpy()
