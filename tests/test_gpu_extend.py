@@ -7,6 +7,7 @@ import torch
 import workloads
 from oracle import attention as o_att
 from oracle import fp8 as o_fp8
+from oracle import layout as o_layout
 from oracle import nvfp4 as o_nv
 from tests import helpers as H
 
@@ -204,8 +205,10 @@ def test_extend_chain_from_nvfp4_cache(nv):
 
 def test_extend_full_size_sampled(nv):
     """The bench's extend workload at full size (16384-token NVFP4 prefix + 2048-token chunk, 8 KV /
-    32 query heads, one NVFP4 layer) through the same calls the bench makes; the oracle recomputes
-    sampled chunk rows (all heads) from the same seeded inputs as decode steps over their visible keys."""
+    32 query heads, one NVFP4 layer) through the same calls the bench makes.  From the same seeded
+    inputs the oracle gives every byte of the NVFP4 prefix cache and of the FP8 workspace (prefix
+    transcoded, chunk appended), both compared whole, and sampled chunk rows (all heads) as decode
+    steps over their visible keys."""
     wl = workloads.config(4)
     layer = 1
     assert not wl.is_fp8(layer)
@@ -234,6 +237,9 @@ def test_extend_full_size_sampled(nv):
     out = nv.fp8_extend_attn(q.to(DEV), c_off, kw, vw, offs, pre, s_wk, s_wv, wl.sm_scale, wl.h_kv, chunk, prefix)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
+    got_kw, got_vw = kw.cpu().numpy(), vw.cpu().numpy()
+    got_pool = {key: a.cpu().numpy() for key, a in pool.items()}
+    del pool, kw, vw
     print("extend full size: GPU done", flush=True)
     # oracle chain on the same inputs
     kpn, vpn = kp.float().numpy(), vp.float().numpy()
@@ -242,10 +248,19 @@ def test_extend_full_size_sampled(nv):
     sw_k, sw_v = np.float32(6.0) * g_k, np.float32(6.0) * g_v
     ck, sck = o_nv.quantize_blocks(kpn, g_k)
     cv, scv = o_nv.quantize_blocks(vpn, g_v)
-    k_hat = np.concatenate([o_fp8.fp8_dequantize(o_fp8.nvfp4_to_fp8_workspace(ck, sck, g_k, sw_k), sw_k),
-                            o_fp8.fp8_dequantize(o_fp8.fp8_quantize(kc.float().numpy(), sw_k), sw_k)])
-    v_hat = np.concatenate([o_fp8.fp8_dequantize(o_fp8.nvfp4_to_fp8_workspace(cv, scv, g_v, sw_v), sw_v),
-                            o_fp8.fp8_dequantize(o_fp8.fp8_quantize(vc.float().numpy(), sw_v), sw_v)])
+    slots = ext.slots(0, 0, prefix)
+    for name, kind, codes, scales in (("K", "k", ck, sck), ("V", "v", cv, scv)):
+        gc, gs = o_layout.read_nvfp4_tokens(got_pool[kind + "_data"], got_pool[kind + "_scale"], kind, slots)
+        assert np.array_equal(gc, codes), f"prefix cache {name} codes differ from the oracle's"
+        assert np.array_equal(gs, scales), f"prefix cache {name} scales differ from the oracle's"
+    want_kw = np.concatenate([o_fp8.nvfp4_to_fp8_workspace(ck, sck, g_k, sw_k), o_fp8.fp8_quantize(kc.float().numpy(), sw_k)])
+    want_vw = np.concatenate([o_fp8.nvfp4_to_fp8_workspace(cv, scv, g_v, sw_v), o_fp8.fp8_quantize(vc.float().numpy(), sw_v)])
+    assert np.array_equal(got_kw, want_kw), f"K workspace: {int((got_kw != want_kw).sum())} bytes differ"
+    assert np.array_equal(got_vw, want_vw), f"V workspace: {int((got_vw != want_vw).sum())} bytes differ"
+    print(f"extend full size: every prefix cache byte and all {want_kw.size + want_vw.size} workspace bytes bit-exact",
+          flush=True)
+    k_hat = o_fp8.fp8_dequantize(want_kw, sw_k)
+    v_hat = o_fp8.fp8_dequantize(want_vw, sw_v)
     qn = q.float().numpy()
     rows = [0, 1, 31, 32, 777, 1024, 2046, 2047] + list(rng.integers(0, chunk, 8))
     want = np.stack([o_att.decode_attention_one(qn[i], k_hat[:prefix + i + 1], v_hat[:prefix + i + 1], wl.sm_scale)
