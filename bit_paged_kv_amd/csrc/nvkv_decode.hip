@@ -287,12 +287,6 @@ __device__ __forceinline__ int wave_max(int v) {
   for (int d = 1; d < 64; d <<= 1) v = max(v, __shfl_xor(v, d, 64));
   return __builtin_amdgcn_readfirstlane(v);
 }
-// Sum across the 64 lanes of a wave, returned as a wave-uniform (scalar) value.
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
-  return __builtin_amdgcn_readfirstlane(v);
-}
 
 // ---- merge of a stream's partials, by the last of its pieces to publish ----
 // Workspace of a decode with several pieces: partial outputs [slots][group][128] fp32, (max, sum)

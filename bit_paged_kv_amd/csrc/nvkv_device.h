@@ -185,8 +185,6 @@ __device__ __forceinline__ uint32_t nvfp4_quantize_block_packed(const float (&x)
 // ---------------------------------------------------------------------------------------------
 // Input loaders
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
 // 8 bf16 values packed in a uint4 -> fp32 (exact)
 __device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float* out) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -219,8 +217,7 @@ __device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// Wave-wide (64 lanes) butterfly reductions over the lanes that differ in the given xor bits.
+// Wave-wide (64 lanes) butterfly maximum over the lanes that differ in the given xor bits.
 __device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
-__device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
 
 }  // namespace nvkv
