@@ -122,10 +122,13 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
 
 /*
  * Split planning for decode.  The step's work -- the pages of every (sequence b, kv head h) stream,
- * in that order -- is cut into num_splits equal pieces, one workgroup of four wavefronts each.
- * When the sequence lengths differ, each stream is also charged a fixed cost of 32 pages (the
+ * in that order -- is cut into num_splits pieces of equal cost, one workgroup of four wavefronts
+ * each.  When the sequence lengths differ, each stream is also charged a fixed cost of 32 pages (the
  * start-up of a segment), so a piece that holds many short streams gets fewer pages.  A piece
- * takes max(pages_per_split, the even ceiling of the step's cost / num_splits) units.
+ * takes max(pages_per_split, the even ceiling of the step's cost / num_splits) units.  When the
+ * lengths are equal and num_splits is even, pieces 2k and 2k + 1 (the two workgroups that share a
+ * compute unit) split their two pieces' units 9 : 7, the larger part going to the workgroup the
+ * hardware dispatches first.
  * A workgroup walks the streams its piece holds: the four wavefronts split each stream's part
  * and combine in LDS.  A stream that lies in one piece is written out directly.  A stream split
  * over several pieces leaves one partial softmax state per piece.  The last of those pieces to
