@@ -5,9 +5,11 @@
 // the fly instead of materialising a dequantized copy.  The Blackwell kernel described there
 // stages tiles in shared memory and converts E2M1 pairs to bf16; this one is designed for gfx950:
 //
-//  * the step's pages are cut into equal pieces, one workgroup of four wavefronts each; a wavefront
-//    owns a quarter of each stream's part of its piece and consumes pages two at a time (32
-//    tokens = the K depth of one v_mfma_f32_16x16x32_f16);
+//  * the step's pages are cut into pieces of equal cost, one workgroup of four wavefronts each (on
+//    a ragged batch every stream also costs a fixed start-up; on equal lengths the two pieces of
+//    the two workgroups that share a compute unit are split 9 : 7); a wavefront owns a quarter of
+//    each stream's part of its piece and consumes pages two at a time (32 tokens = the K depth of
+//    one v_mfma_f32_16x16x32_f16);
 //  * every lane issues one 16-byte load per page for K and one for V (the in-page byte layout puts
 //    each lane's MFMA operand in 16 contiguous bytes), plus its scale bytes -- no LDS staging;
 //  * E2M1 pairs and E4M3 scale pairs become fp16 with the gfx950 pair converts; e2m1 * scale is

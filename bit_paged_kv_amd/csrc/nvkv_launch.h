@@ -35,9 +35,9 @@ hipError_t launch_extend_attn(const void* q, const int32_t* chunk_offsets, const
                               float v_ws_scale, float sm_scale, int batch, int hq, int hkv, int max_chunk,
                               float* out, hipStream_t stream);
 
-// Decode: the step's pages are cut into num_splits equal pieces, one workgroup of four wavefronts
-// each; a stream split over several pieces leaves partial softmax states that the last of its
-// pieces to finish merges.
+// Decode: the step's pages are cut into num_splits pieces of equal cost, one workgroup of four
+// wavefronts each; a stream split over several pieces leaves partial softmax states that the last
+// of its pieces to finish merges.
 enum CacheFormat { kFmtNvfp4 = 0, kFmtFp8 = 1 };
 
 struct DecodeArgs {
