@@ -69,7 +69,7 @@ def test_plan_pieces(lib, b, hkv, L, tot):
 
 def test_plan_shapes(lib):
     """The planner's shapes on a 256-CU device (the count it assumes without a GPU, and MI355X's):
-    two equal pieces per CU whenever the step has at least 512 x 16 page-heads; on equal lengths
+    two pieces of equal cost per CU whenever the step has at least 512 x 16 page-heads; on equal lengths
     whose stream count divides 512 the pieces fall on stream boundaries (the kernel's piece is
     the even ceiling of units / pieces)."""
     for args, pieces_per_stream in (((4, 8, 131072, 4 * 131072), 16), ((32, 8, 4096, 32 * 4096), 2)):
