@@ -290,6 +290,42 @@ def test_decode_layers_mixed_stack(nv):
             assert torch.equal(L["out"], first[i]), f"prepared layer {i}"
 
 
+def _random_case(i):
+    """A seeded random decode shape: batch, kv heads, group size (1..16, not only powers of two),
+    equal, ragged or mostly one-token lengths, fused append or not, and an automatic or forced plan.
+    The whole cache stays under ~80k token-heads so the oracle finishes in about a second."""
+    rng = np.random.default_rng(9000 + i)
+    batch = int(rng.choice([1, 2, 3, 7, 31, 64, 65, 100, 140]))
+    h_kv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16]))
+    kind = int(rng.integers(0, 3))
+    budget = 80_000 // h_kv
+    if kind == 0:
+        lens = [int(rng.integers(1, max(2, budget // batch)))] * batch
+    else:
+        lens = rng.integers(1, max(2, min(4000, 2 * budget // batch)), size=batch)
+        if kind == 2:
+            lens[rng.random(batch) < 0.3] = 1
+    wl = workloads.Workload(name=f"random-{i}", seed=9100 + i, batch=batch, h_kv=h_kv, h_q=h_kv * group,
+                            seq_lens=lens, append=bool(rng.integers(0, 2)), extra_pages=int(rng.integers(0, 5)))
+    return wl, int(rng.choice([0, 0, 2, 4, 6, 16, 64, 1000]))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_decode_random_shapes(nv, i):
+    wl, pps = _random_case(i)
+    ks, vs = H.oracle_inputs(wl)                        # cache (+ the appended token)
+    gk, gv = H.oracle_nvfp4_scales(wl)                  # from the cache only
+    want = H.oracle_nvfp4_decode(wl, wl.q().float().numpy(), ks, vs, gk, gv)
+    pool, g_k, g_v = H.gpu_nvfp4_layer(wl, 0, DEV)
+    assert (np.float32(g_k), np.float32(g_v)) == (gk, gv)
+    got, plan = _run_nvfp4(nv, wl, pool, g_k, g_v, force_pps=pps, fused=wl.append)
+    tag = (f"random case {i}: batch {wl.batch}, Hkv {wl.h_kv}, G {wl.h_q // wl.h_kv}, tokens {int(wl.total_lens.sum())}, "
+           f"append {wl.append}, plan {plan}")
+    err = H.assert_attention_close(got, want, tag)
+    print(f"{tag}: max-abs {err[0]:.2e} rel-L2 {err[1]:.2e}", flush=True)
+
+
 def _pool_rows(pool, wl, b, hk, n_tok):
     """The pages of stream (b, hk) that hold its first n_tok tokens, copied to the host in sequence
     order: {key: [pages][1][bytes]}, so that token t sits at local slot t."""
