@@ -83,6 +83,53 @@ def test_nvfp4_quantize_ragged_scattered_bitexact(nv):
     _check_pool(pool, want)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_nvfp4_quantize_random_calls_bitexact(nv, case):
+    """A cache written by many calls: every sequence is cut into random consecutive chunks (1 to 200
+    tokens), the chunks are shuffled into calls of one to four chunks, and some calls list their
+    tokens in a random order.  So a call meets V token quads whose other tokens are already in the
+    pool, quads it completes itself, runs crossing the writer's token windows, and input orders
+    unlike the slot order.  The oracle writes the same tokens at the same slots; every pool byte
+    (the 0x3C fill of unused slots included) must match."""
+    rng = np.random.default_rng(700 + case)
+    batch = int(rng.integers(1, 9))
+    h_kv = int(rng.choice([1, 2, 3, 8]))
+    lens = rng.integers(1, 900, size=batch)
+    wl = workloads.Workload(name=f"calls-{case}", seed=710 + case, batch=batch, h_kv=h_kv, h_q=h_kv,
+                            seq_lens=lens, extra_pages=int(rng.integers(0, 4)))
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = H.oracle_nvfp4_scales(wl)
+    want = H.oracle_nvfp4_pool(wl, ks, vs, gk, gv, fill=0x3C)
+    chunks = []
+    for b in range(batch):
+        t = 0
+        while t < lens[b]:
+            n = int(min(lens[b] - t, rng.integers(1, 201)))
+            chunks.append((b, t, t + n))
+            t += n
+    order = [int(c) for c in rng.permutation(len(chunks))]
+    kb = [wl.kv("k", b) for b in range(batch)]
+    vb = [wl.kv("v", b) for b in range(batch)]
+    pool = nv.alloc_nvfp4_pool(wl.num_pages, h_kv, DEV, fill=0x3C)
+    calls = 0
+    while order:
+        m = int(rng.integers(1, 5))
+        sel, order = order[:m], order[m:]
+        k = torch.cat([kb[chunks[c][0]][chunks[c][1]:chunks[c][2]] for c in sel])
+        v = torch.cat([vb[chunks[c][0]][chunks[c][1]:chunks[c][2]] for c in sel])
+        slots = np.concatenate([wl.slots(chunks[c][0], chunks[c][1], chunks[c][2]) for c in sel]).astype(np.int32)
+        if rng.random() < 0.3:
+            p = rng.permutation(len(slots))
+            k, v, slots = k[torch.from_numpy(p)], v[torch.from_numpy(p)], slots[p]
+        nv.nvfp4_quantize_append(k.contiguous().to(DEV), v.contiguous().to(DEV), torch.from_numpy(slots).to(DEV),
+                                 float(gk), float(gv), pool)
+        calls += 1
+    torch.cuda.synchronize()
+    _check_pool(pool, want)
+    print(f"random calls {case}: {batch} sequences, {h_kv} kv heads, {len(chunks)} chunks in {calls} calls: "
+          "every pool byte bit-exact", flush=True)
+
+
 def test_nvfp4_quantize_golden_and_edge_blocks_bitexact(nv):
     """The hand-worked blocks, plus ties, saturation, subnormal and zero scales, signed zeros."""
     gold = json.load(open(os.path.join(GOLD, "nvfp4_worked_blocks.json")))["blocks"]
