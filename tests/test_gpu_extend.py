@@ -88,6 +88,25 @@ def test_extend_attention_matches_oracle(nv, prefixes, chunks, hkv, hq):
     H.assert_attention_close(got, want, f"extend p={prefixes} c={chunks} G={hq // hkv}")
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_extend_attention_random_shapes(nv, case):
+    """Seeded random extend shapes: 1-4 sequences with prefixes 0-3000 and chunks 1-700 tokens
+    (a prefix of 0 is a prefill), 1-8 kv heads and query groups 1-16; sequences of one call differ."""
+    rng = np.random.default_rng(4000 + case)
+    b = int(rng.integers(1, 5))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 11, 16]))
+    prefixes = [int(rng.choice([0, int(rng.integers(1, 3001))])) for _ in range(b)]
+    chunks = [int(rng.integers(1, 701)) for _ in range(b)]
+    sm = 1.0 / np.sqrt(128.0)
+    args = _ws_case(4100 + case, prefixes, chunks, hkv, hkv * group)
+    want = _oracle(*args, prefixes, sm)
+    got = _gpu(nv, *args, prefixes, sm, hkv)
+    err = H.assert_attention_close(got, want, f"extend random {case}: p={prefixes} c={chunks} Hkv={hkv} G={group}")
+    print(f"extend random {case}: p={prefixes} c={chunks} Hkv={hkv} G={group}: max-abs {err[0]:.2e} rel-L2 {err[1]:.2e}",
+          flush=True)
+
+
 def test_extend_attention_rising_maximum(nv):
     """K rows grow ~12x along the sequence, so the running maximum of every column rises again and
     again (each rise rescales the accumulated output); 100 chunk tokens at G = 4 fill both halves of
