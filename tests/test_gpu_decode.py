@@ -252,6 +252,26 @@ def test_fp8_decode(nv, group):
         H.assert_attention_close(got.cpu().numpy(), want, f"fp8 plan={plan}")
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_fp8_decode_random_shapes(nv, i):
+    """FP8 layers on seeded random shapes (as the NVFP4 ones, without the append, which FP8 caches
+    do not have), automatic and forced plans."""
+    import dataclasses
+    from bit_paged_kv_amd import paged
+    wl, pps = _random_case(50 + i)
+    wl = dataclasses.replace(wl, name=f"fp8-random-{i}", append=False)
+    want, sk, sv = _fp8_case(wl)
+    k, v, slots = H.gpu_all_tokens(wl, 0, DEV)
+    pool, g_sk, g_sv = paged.build_fp8_cache(k, v, slots, wl.num_pages, fill=0xFF)
+    assert (np.float32(g_sk), np.float32(g_sv)) == (sk, sv)
+    pt, sl = H.gpu_tables(wl, DEV)
+    plan = nv.plan_decode(wl.batch, wl.h_kv, int(wl.total_lens.max()), int(wl.total_lens.sum()), pps)
+    got = nv.fp8_decode(wl.q().to(DEV), pool, g_sk, g_sv, pt, sl, wl.sm_scale, plan, wl.h_kv)
+    tag = f"fp8 random case {i}: batch {wl.batch}, Hkv {wl.h_kv}, G {wl.h_q // wl.h_kv}, plan {plan}"
+    err = H.assert_attention_close(got.cpu().numpy(), want, tag)
+    print(f"{tag}: max-abs {err[0]:.2e} rel-L2 {err[1]:.2e}", flush=True)
+
+
 def test_decode_layers_mixed_stack(nv):
     from bit_paged_kv_amd import paged
     wl = workloads.Workload(name="mixed-small", seed=70, batch=3, h_kv=2, h_q=8, seq_lens=[64, 300, 17],

@@ -382,3 +382,43 @@ def test_dequant_to_workspace_bitexact(nv, case):
         call.run()
         assert np.array_equal(kw2.cpu().numpy(), want_k)
         assert np.array_equal(vw2.cpu().numpy(), want_v)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_dequant_to_workspace_random_bitexact(nv, case):
+    """The prefix gather on seeded random shapes: 1-6 sequences, prefixes of 0 up to the whole
+    sequence, gaps between the workspace rows of consecutive sequences, 1-8 kv heads; every
+    workspace byte (the untouched 0xEE rows included) against the oracle's transcode."""
+    rng = np.random.default_rng(800 + case)
+    batch = int(rng.integers(1, 7))
+    h_kv = int(rng.choice([1, 2, 3, 8]))
+    lens = rng.integers(1, 2500, size=batch)
+    wl = workloads.Workload(name=f"ws-random-{case}", seed=810 + case, batch=batch, h_kv=h_kv, h_q=h_kv,
+                            seq_lens=lens, extra_pages=int(rng.integers(0, 4)))
+    prefix = np.array([int(rng.choice([0, int(rng.integers(0, n + 1)), n])) for n in lens], dtype=np.int32)
+    gaps = rng.integers(0, 9, size=batch)
+    offs = np.concatenate([[0], np.cumsum(prefix + gaps)]).astype(np.int32)
+    rows = int(offs[-1]) + 2
+    ks, vs = H.oracle_inputs(wl)
+    gk, gv = o_nv.global_scale(np.concatenate(ks)), o_nv.global_scale(np.concatenate(vs))
+    s_wk, s_wv = np.float32(6.0) * gk, np.float32(6.0) * gv
+    want_k = np.full((rows, h_kv, 128), 0xEE, np.uint8)
+    want_v = want_k.copy()
+    for b in range(batch):
+        n = int(prefix[b])
+        if n == 0:
+            continue
+        ck, sck = o_nv.quantize_blocks(ks[b][:n], gk)
+        cv, scv = o_nv.quantize_blocks(vs[b][:n], gv)
+        want_k[offs[b]:offs[b] + n] = o_fp8.nvfp4_to_fp8_workspace(ck, sck, gk, s_wk)
+        want_v[offs[b]:offs[b] + n] = o_fp8.nvfp4_to_fp8_workspace(cv, scv, gv, s_wv)
+    pool, _, _ = H.gpu_nvfp4_layer(wl, 0, DEV)
+    kw = torch.full((rows, h_kv, 128), 0xEE, dtype=torch.uint8, device=DEV)
+    vw = kw.clone()
+    nv.dequant_to_workspace(pool, float(gk), float(gv), torch.from_numpy(wl.page_table).to(DEV),
+                            torch.from_numpy(prefix).to(DEV), torch.from_numpy(offs).to(DEV), int(prefix.max()),
+                            float(s_wk), float(s_wv), h_kv, kw, vw)
+    torch.cuda.synchronize()
+    assert np.array_equal(kw.cpu().numpy(), want_k), f"case {case}: K workspace differs"
+    assert np.array_equal(vw.cpu().numpy(), want_v), f"case {case}: V workspace differs"
+
