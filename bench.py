@@ -130,11 +130,10 @@ def host_cpu():
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch, one counter per run) scaled by
 # the factors a plain 1 GiB device copy gives (x2.000 / x1.000).  Valid only for the kernel sources
 # (the decode file and the headers it includes, hashed together) and the split plan they were taken
-# with; reported as null otherwise.  (Taken at sha256 76fa8448de4f61cd...; the sources since changed only
-# in comments and three helpers the kernels never called: identical machine code for every decode kernel.)
+# with; reported as null otherwise.
 TRAFFIC = {
-    "long": {"source_sha256": "ef2becbf1f24de59518f8748b949b6e7012e9d4c243c9feed6a0225d687c6816", "plan": [2, 512],
-             "kernels": {"decode_split_kernel": (296439.2, 4304.0)},
+    "long": {"source_sha256": "fee6281dd19eaf7d4fa29e105df3dff8e37ae6031ca0c2b3352b6b397c023ed5", "plan": [2, 512],
+             "kernels": {"decode_split_kernel": (296438.7, 4304.0)},
              "fetch_factor": 2.0, "write_factor": 1.0},
 }
 

@@ -66,9 +66,10 @@ size_t decode_workspace_bytes(int batch, int hq, int hkv, int num_splits);
 unsigned next_decode_gen();
 
 // Cost, in pages, that the decode partition charges for each stream of a batch whose lengths
-// differ: the start-up of a segment (two memory round trips and the combine) measured against the
-// time a workgroup takes per page.
-constexpr int kStreamCostPages = 32;
+// differ: the start-up of a segment (two memory round trips and the combine) against the time a
+// workgroup takes per page.  Swept on a 64-sequence ragged batch: 16 pages 134.2-134.7 us per
+// step, 32 126.3-126.7, 48 124.7-125.2, 64 125.1-125.9.
+constexpr int kStreamCostPages = 48;
 
 // Split partials held by the library for the no-allocation decode entry point: a 32 MiB array per
 // device, room for 64,527 partial rows of 130 floats (e.g. 7553 pieces + 512 streams of 8 query

@@ -123,7 +123,7 @@ NVKV_API int fp8_kv_quantize_append(const void* k_in, const void* v_in, const in
 /*
  * Split planning for decode.  The step's work -- the pages of every (sequence b, kv head h) stream,
  * in that order -- is cut into num_splits pieces of equal cost, one workgroup of four wavefronts
- * each.  When the sequence lengths differ, each stream is also charged a fixed cost of 32 pages (the
+ * each.  When the sequence lengths differ, each stream is also charged a fixed cost of 48 pages (the
  * start-up of a segment), so a piece that holds many short streams gets fewer pages.  A piece
  * takes max(pages_per_split, the even ceiling of the step's cost / num_splits) units.  When the
  * lengths are equal and num_splits is even, pieces 2k and 2k + 1 (the two workgroups that share a
@@ -173,7 +173,7 @@ NVKV_API size_t nvkv_decode_workspace_size(int batch, int num_q_heads, int num_k
  *   page_table : [batch][max_pages_per_seq] int32, device.
  *   seq_lens   : [batch] int32, device, each >= 1 and <= max_pages_per_seq * 16 (includes the
  *                appended token when new_k != NULL).  NVKV_E_UNSUPPORTED when
- *                batch * (max_pages_per_seq + 32) * num_kv_heads + 2 * num_splits or
+ *                batch * (max_pages_per_seq + 48) * num_kv_heads + 2 * num_splits or
  *                num_splits * pages_per_split exceeds 2^31 - 1 (32-bit unit offsets).
  *   num_q_heads / num_kv_heads must be an integer in 1..16.
  *   pages_per_split, num_splits : from nvkv_plan_decode.
