@@ -495,7 +495,7 @@ int fp8_extend_attn(const void* q, const int32_t* chunk_offsets, const uint8_t* 
   if (max_chunk_len == 0) return NVKV_OK;
   return launch_status(nvkv::launch_extend_attn(q, chunk_offsets, k_ws, v_ws, ws_offsets, prefix_lens, k_ws_scale,
                                                 v_ws_scale, sm_scale, batch, num_q_heads, num_kv_heads,
-                                                max_chunk_len, out, stream));
+                                                max_chunk_len, device_cus(), out, stream));
 }
 
 int nvkv_read_probe(const void* buf, size_t bytes, unsigned* sink, hipStream_t stream) {

@@ -6,8 +6,10 @@
 // prefix into a shared FP8 workspace and attends over it.  Unlike decode this is compute-bound (the
 // chunk's queries share every key), so the design centres on keeping the matrix cores busy:
 //
-//  * one workgroup of eight waves per (sequence, kv head, block of query tokens); its 256 score
-//    columns are (query token, query head of the group) pairs, 32 per wave, so every K/V tile
+//  * one workgroup of eight waves per (sequence, kv head, block of query tokens); its 256 or 384
+//    score columns are (query token, query head of the group) pairs, 32 or 48 per wave (two or three
+//    16-column tiles: three when the grid is long enough to fill the device anyway, since each K/V
+//    operand read from LDS then serves 1.5x the columns), so every K/V tile
 //    staged in LDS serves all G query heads of the kv head;
 //  * the waves form two groups of four (one wave of each on every SIMD) that alternate between a
 //    matrix phase (S = K Q^T for tile i and O += V P for tile i - 1) and a vector phase (the online
@@ -37,7 +39,6 @@ namespace nvkv {
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
 constexpr int kXWaves = 8;               // two groups of four
-constexpr int kXCols = 32 * kXWaves;     // score columns per workgroup
 constexpr int kXKeys = 32;               // keys per tile
 constexpr int kKRow = 128 + 8;           // bf16 elements per K row in LDS (16-byte pad: conflict-free reads)
 // V in LDS: [g][channel][8 keys] fp16 with keys 4 g .. 4 g + 3 then 16 + 4 g .. 16 + 4 g + 3 of the tile,
@@ -116,6 +117,8 @@ struct ExtendArgs {
   float* out;                   // fp32 [total_q][hq][128]
 };
 
+// kCT: 16-column score tiles per wave (2 or 3)
+template <int kCT>
 __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[3][kXKeys * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[3][4 * kVGroup];
@@ -152,22 +155,22 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
 
   // ---- this lane's two score columns (one per 16-column tile) ----
   const int g = lane >> 4, col16 = lane & 15;
-  bf8v qop[2][4];      // B operands of S^T = K Q^T: Q^T[32 ks + 8 g .. + 7][column]
+  bf8v qop[kCT][4];      // B operands of S^T = K Q^T: Q^T[32 ks + 8 g .. + 7][column]
   // Per-column facts, recomputed where they are needed (the diagonal tiles, the epilogue) rather
   // than kept in registers through the main loop: lim = keys < lim are visible to the column (0 for
   // a padding column), row = element offset of its q row (and of its output row).
   auto col_lim = [&](int ct, int l16) -> int {
-    const int tk = (32 * wave + 16 * ct + l16) / a.group;
+    const int tk = (16 * kCT * wave + 16 * ct + l16) / a.group;
     const int qt = qt0 + tk;
     return (tk < a.tokens_per_wg && qt < chunk) ? prefix + qt + 1 : 0;
   };
   auto col_row = [&](int ct, int l16) -> size_t {
-    const int c = 32 * wave + 16 * ct + l16;
+    const int c = 16 * kCT * wave + 16 * ct + l16;
     const int tk = c / a.group, hc = c - tk * a.group;
     return ((size_t)(row0 + qt0 + tk) * a.hq + (size_t)hk * a.group + hc) * 128;
   };
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < kCT; ++ct) {
     const bool ok = col_lim(ct, col16) != 0;
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + (ok ? col_row(ct, col16) : 0));
 #pragma unroll
@@ -238,24 +241,32 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
   // have seen no visible key yet (their weights are exp2(-inf) = 0, and the first real maximum
   // rescales the empty state by exp2(-1e30 - m) = 0)
   constexpr float kFloor = -1.0e30f;
-  float m_run[2] = {kFloor, kFloor}, l_run[2] = {0.0f, 0.0f};
-  f4 o[8][2];
+  float m_run[kCT], l_run[kCT];
+  f4 o[8][kCT];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) o[n][0] = o[n][1] = f4{0.f, 0.f, 0.f, 0.f};
-  f4 s[2][2];          // scores of the tile awaiting its softmax: rows are keys 16 rt + 4 g + r
-  h8 phi[2], plo[2];   // B operands of PV for the tile awaiting it: P^T hi / lo
+  for (int ct = 0; ct < kCT; ++ct) {
+    m_run[ct] = kFloor;
+    l_run[ct] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) o[n][ct] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  f4 s[2][kCT];          // scores of the tile awaiting its softmax: rows are keys 16 rt + 4 g + r
+  h8 phi[kCT], plo[kCT];   // B operands of PV for the tile awaiting it: P^T hi / lo
   // A raise of the running maximum rescales O by alpha.  The vector phase only records alpha; the
   // next matrix phase applies it before its PV products, so O is only ever updated in matrix phases.
-  float alpha_pend[2] = {1.0f, 1.0f};
+  float alpha_pend[kCT];
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct) alpha_pend[ct] = 1.0f;
   bool rescale_pend = false;   // wave-uniform
   auto apply_rescale = [&]() {
     if (rescale_pend) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        o[n][0] *= alpha_pend[0];
-        o[n][1] *= alpha_pend[1];
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) o[n][ct] *= alpha_pend[ct];
       }
-      alpha_pend[0] = alpha_pend[1] = 1.0f;   // a later raise of one column tile leaves the other at 1
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) alpha_pend[ct] = 1.0f;   // a later raise of one column tile leaves the other at 1
       rescale_pend = false;
     }
   };
@@ -285,18 +296,19 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
     }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      s[rt][0] = s[rt][1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        s[rt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[rt][ks], qop[0][ks], s[rt][0], 0, 0, 0);
-        s[rt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[rt][ks], qop[1][ks], s[rt][1], 0, 0, 0);
-      }
+      for (int ct = 0; ct < kCT; ++ct) s[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct)
+          s[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[rt][ks], qop[ct][ks], s[rt][ct], 0, 0, 0);
     }
     if constexpr (kPV) {
 #pragma unroll
       for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < kCT; ++ct) {
           o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[n], phi[ct], o[n][ct], 0, 0, 0);
           o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[n], plo[ct], o[n][ct], 0, 0, 0);
         }
@@ -313,7 +325,7 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
       const h8 vop =
           __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(&v_lds[vb][g * kVGroup + (16 * n + col16) * 8]));
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < kCT; ++ct) {
         o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, phi[ct], o[n][ct], 0, 0, 0);
         o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, plo[ct], o[n][ct], 0, 0, 0);
       }
@@ -324,7 +336,7 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
     const int key0 = tile * kXKeys;
     const bool edge = key0 + kXKeys > prefix + qt0;   // some column may not see every key of the tile
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < kCT; ++ct) {
       float x[8];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
@@ -428,7 +440,7 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
 
   // ---- normalise and write: lane holds O^T[16 n + 4 g + r][column] ----
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < kCT; ++ct) {
     const float l = xsum32(xsum16(l_run[ct]));
     if (col_lim(ct, lane_here() & 15) == 0) continue;
     const float f = a.v_scale / l;
@@ -441,7 +453,7 @@ __global__ __launch_bounds__(64 * kXWaves, 2) void extend_attn_kernel(ExtendArgs
 hipError_t launch_extend_attn(const void* q, const int32_t* q_offsets, const uint8_t* k_ws, const uint8_t* v_ws,
                               const int32_t* ws_offsets, const int32_t* prefix_lens, float k_ws_scale,
                               float v_ws_scale, float sm_scale, int batch, int hq, int hkv, int max_chunk,
-                              float* out, hipStream_t stream) {
+                              int cus, float* out, hipStream_t stream) {
   ExtendArgs a;
   a.q = reinterpret_cast<const uint16_t*>(q);
   a.q_offsets = q_offsets;
@@ -455,11 +467,22 @@ hipError_t launch_extend_attn(const void* q, const int32_t* q_offsets, const uin
   a.hq = hq;
   a.hkv = hkv;
   a.group = hq / hkv;
-  a.tokens_per_wg = kXCols / a.group;
+  // Three 16-column tiles per wave when that grid still gives every compute unit four workgroups or
+  // more (each LDS operand read then serves 1.5x the columns: a 16384-token prefill, 62.5 against
+  // 64.5 ms per 24 layers side by side); two otherwise, where fewer, wider workgroups would leave
+  // units idle (a 2048-token chunk over 8 kv heads: 171 workgroups for 256 units, 24.8 against
+  // 18.0 ms).
+  const int tpw3 = 16 * 3 * kXWaves / a.group;
+  const long long grid3 = (long long)((max_chunk + tpw3 - 1) / tpw3) * hkv * batch;
+  const int ct = grid3 >= 4LL * cus ? 3 : 2;
+  a.tokens_per_wg = 16 * ct * kXWaves / a.group;
   a.n_blocks = (max_chunk + a.tokens_per_wg - 1) / a.tokens_per_wg;
   a.out = out;
   dim3 grid((unsigned)a.n_blocks * hkv, batch);
-  hipLaunchKernelGGL(extend_attn_kernel, grid, dim3(64 * kXWaves), 0, stream, a);
+  if (ct == 3)
+    hipLaunchKernelGGL(extend_attn_kernel<3>, grid, dim3(64 * kXWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(extend_attn_kernel<2>, grid, dim3(64 * kXWaves), 0, stream, a);
   return hipGetLastError();
 }
 

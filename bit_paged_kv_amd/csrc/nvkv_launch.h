@@ -33,7 +33,7 @@ hipError_t launch_fp8_ws_append(const void* k, const void* v, const int32_t* chu
 hipError_t launch_extend_attn(const void* q, const int32_t* chunk_offsets, const uint8_t* k_ws, const uint8_t* v_ws,
                               const int32_t* ws_offsets, const int32_t* prefix_lens, float k_ws_scale,
                               float v_ws_scale, float sm_scale, int batch, int hq, int hkv, int max_chunk,
-                              float* out, hipStream_t stream);
+                              int cus, float* out, hipStream_t stream);
 
 // Decode: the step's pages are cut into num_splits pieces of equal cost, one workgroup of four
 // wavefronts each; a stream split over several pieces leaves partial softmax states that the last

@@ -68,7 +68,7 @@ hipError_t launch_fp8_ws_append(const void*, const void*, const int32_t*, const 
   return hipSuccess;
 }
 hipError_t launch_extend_attn(const void*, const int32_t*, const uint8_t*, const uint8_t*, const int32_t*,
-                              const int32_t*, float, float, float, int, int, int, int, float*, hipStream_t) {
+                              const int32_t*, float, float, float, int, int, int, int, int, float*, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }

@@ -107,6 +107,29 @@ def test_extend_attention_random_shapes(nv, case):
           flush=True)
 
 
+@pytest.mark.parametrize("batch,hkv,group,chunk_range", [
+    (128, 8, 4, (30, 91)),      # 96 tokens per workgroup: one block per sequence, 1024 workgroups
+    (64, 8, 16, (30, 71)),      # 24 tokens per workgroup: two or three blocks per sequence
+    (130, 8, 5, (50, 151)),     # 76 tokens per workgroup and four padding columns
+    (128, 8, 3, (60, 129)),     # 128 tokens per workgroup
+    (256, 4, 1, (200, 384)),    # 384 tokens per workgroup
+])
+def test_extend_attention_wide_tiles(nv, batch, hkv, group, chunk_range):
+    """Grids long enough (at least four workgroups per compute unit on a 256-unit device) for the
+    launcher to pick three 16-column score tiles per wave; ragged prefixes and chunks."""
+    rng = np.random.default_rng(batch * 31 + group)
+    prefixes = [int(x) for x in rng.integers(0, 200, size=batch)]
+    chunks = [int(x) for x in rng.integers(chunk_range[0], chunk_range[1], size=batch)]
+    tpw3 = 384 // group
+    assert -(-max(chunks) // tpw3) * hkv * batch >= 4 * 256
+    sm = 1.0 / np.sqrt(128.0)
+    args = _ws_case(5000 + batch + group, prefixes, chunks, hkv, hkv * group, pad=1)
+    want = _oracle(*args, prefixes, sm)
+    got = _gpu(nv, *args, prefixes, sm, hkv)
+    err = H.assert_attention_close(got, want, f"extend wide tiles B={batch} Hkv={hkv} G={group}")
+    print(f"extend wide tiles B={batch} Hkv={hkv} G={group}: max-abs {err[0]:.2e} rel-L2 {err[1]:.2e}", flush=True)
+
+
 def test_extend_attention_rising_maximum(nv):
     """K rows grow ~12x along the sequence, so the running maximum of every column rises again and
     again (each rise rescales the accumulated output); 100 chunk tokens at G = 4 fill both halves of
